@@ -1,0 +1,390 @@
+"""Bench: paged chunked-prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras] [--no-cpu]
+
+One step = one pass of the hot path over the headline workload: a
+Llama-3-8B attention layer (32 q / 8 kv heads, d=128, bf16, 128-token
+pages) taking one 512-token chunk at each prefix H in {0, 4096, 8192,
+12288} (the history sweep of the dynamic-chunking design's problem
+statement; 512-token chunks of the vLLM chunked-prefill article): for each
+H, the chunk's K/V are written into the paged cache through slot_mapping,
+then attention runs over prefix + chunk. Metadata planning and upload
+happen once per workload, outside the timed region (a plan serves every
+layer of a batch step). Inputs are resident in HBM before timing starts.
+
+The printed JSON line (last line of stdout) carries:
+  value      -- algorithmic TFLOP/s of the whole step (KV writes included),
+                FLOP per chunk = 4*Hq*d*C*(H + C/2);
+  roofline   -- the attention call (prefill MFMA kernel + split combine)
+                against bf16 dense MFMA peak, averaged over the four H;
+  decode     -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
+                40/40 heads): algorithmic K+V+Q+O bytes / time vs HBM peak;
+  cpu_baseline -- the fp64 oracle on a bounded sample of the H=12288 chunk.
+--extras adds the mixed batch, the 70B-like long-context sweep and the
+chunk-size predictor run as extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+HIST_SWEEP = (0, 4096, 8192, 12288)
+CHUNK = 512
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_chunk(hq, d, c, h):
+    return 4.0 * hq * d * c * (h + c / 2.0)
+
+
+def median_ms(fn, reps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    t = sorted(s.elapsed_time(e) for s, e in ev)
+    return {"median_ms": t[len(t) // 2], "p10_ms": t[len(t) // 10], "p90_ms": t[(9 * len(t)) // 10],
+            "mean_ms": sum(t) / len(t)}
+
+
+# ---------------------------------------------------------------------------
+def headline(args):
+    import torch
+    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+
+    dbs = []
+    for h in HIST_SWEEP:
+        b = llama3_8b_chunk(h)
+        db = DeviceBatch(b)
+        dbs.append((h, db))
+        log(f"[bench] llama3-8b C{CHUNK} H{h}: plan {db.plan.info()}")
+    hq, d = 32, 128
+    flops = [flops_chunk(hq, d, CHUNK, h) for h in HIST_SWEEP]
+
+    def step():
+        for _, db in dbs:
+            db.kv_write()
+            db.attention()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Per-call events on the launch stream (torch's current stream), inside
+    # the timed region.
+    n = len(dbs)
+    ev_attn = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)] for _ in range(n)]
+    ev_kv = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for i, (_, db) in enumerate(dbs):
+            ev_kv[i][k][0].record()
+            db.kv_write()
+            ev_kv[i][k][1].record()
+            ev_attn[i][k][0].record()
+            db.attention()
+            ev_attn[i][k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_h = []
+    attn_ms_tot = 0.0
+    for i, h in enumerate(HIST_SWEEP):
+        a = sorted(s.elapsed_time(e) for s, e in ev_attn[i])
+        kv = sorted(s.elapsed_time(e) for s, e in ev_kv[i])
+        am = sum(a) / len(a)
+        attn_ms_tot += am
+        per_h.append({"H": h, "attn_us_mean": am * 1e3, "attn_us_median": a[len(a) // 2] * 1e3,
+                      "kv_write_us_mean": sum(kv) / len(kv) * 1e3,
+                      "tflops": flops[i] / (am * 1e-3) / 1e12,
+                      "mfma_frac": flops[i] / (am * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+        log(f"[bench] H={h}: attention {am*1e3:.1f} us -> {per_h[-1]['tflops']:.1f} TFLOP/s "
+            f"({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak); kv_write "
+            f"{per_h[-1]['kv_write_us_mean']:.1f} us")
+    ms_per_step = wall * 1e3 / args.steps
+    total_flops = sum(flops)
+    achieved = (total_flops / n) / (attn_ms_tot / n * 1e-3) / 1e12
+    return {
+        "ms_per_step": ms_per_step,
+        "value": total_flops / (ms_per_step * 1e-3) / 1e12,
+        "per_H": per_h,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None,
+                     "kernel": "cpa_attention (prefill_kernel<128> + combine_kernel<128>)",
+                     "flop_per_launch": total_flops / n},
+    }
+
+
+def decode_rows(args, mixed):
+    """LLaMA-13B decode rows alone: a plan over the 16 query_len-1 rows of
+    the mixed batch (its prefill chunks get query_len 0)."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    b, db = mixed
+    nd = 16
+    ql = [1] * nd + [0] * (b.num_seqs - nd)
+    plan = cpa.cpa_plan_create(db.desc, ql, b.seq_lens)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    cpa.cpa_plan_upload(plan, ws)
+    q = db.q[:nd]
+    out = db.out[:nd]
+    r = median_ms(lambda: cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table,
+                                            out, ws), args.decode_reps, 5)
+    hkv, d = b.num_kv_heads, b.head_dim
+    kv_bytes = float(sum(int(n) for n in b.seq_lens[:nd])) * hkv * d * 2 * 2
+    qo_bytes = nd * b.num_q_heads * d * 2 * 2
+    gbs = (kv_bytes + qo_bytes) / (r["mean_ms"] * 1e-3) / 1e9
+    res = {"workload": "llama13b 16 decode rows, seq_len U[1024,8192], 40/40 heads, d=128",
+           "bytes": kv_bytes + qo_bytes, "us_mean": r["mean_ms"] * 1e3,
+           "us_median": r["median_ms"] * 1e3, "GB_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+           "plan": plan.info()}
+    log(f"[bench] decode rows: {res['us_mean']:.1f} us, {gbs:.0f} GB/s "
+        f"({100*gbs/HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return res
+
+
+def mixed_extras(args, mixed):
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    b, db = mixed
+    r_all = median_ms(lambda: db.attention(), args.decode_reps, 3)
+    nd = 16
+    ql = [0] * nd + [int(x) for x in b.query_lens[nd:]]
+    plan = cpa.cpa_plan_create(db.desc, ql, b.seq_lens)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    cpa.cpa_plan_upload(plan, ws)
+    r_pf = median_ms(lambda: cpa.cpa_attention(plan, db.q[nd:], db.k_cache, db.v_cache,
+                                               db.block_table, db.out[nd:], ws),
+                     args.decode_reps, 3)
+    pf_flops = sum(flops_chunk(40, 128, int(c), int(n) - int(c))
+                   for c, n in zip(b.query_lens[nd:], b.seq_lens[nd:]))
+    res = {"mixed_call_us": r_all["mean_ms"] * 1e3,
+           "prefill_only_us": r_pf["mean_ms"] * 1e3,
+           "prefill_only_tflops": pf_flops / (r_pf["mean_ms"] * 1e-3) / 1e12}
+    log(f"[bench] llama13b mixed call {res['mixed_call_us']:.1f} us; prefill chunks alone "
+        f"{res['prefill_only_us']:.1f} us = {res['prefill_only_tflops']:.1f} TFLOP/s")
+    return res
+
+
+def long_context(args):
+    """70B-like layer (64 q / 8 kv heads): one 32768-token prompt prefilled in
+    16 chunks of 2048; each chunk = KV write + attention."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+    b = make_batch(5, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=128,
+                   query_lens=[32768], seq_lens=[32768])
+    db = DeviceBatch(b)
+    rows = []
+    tot_f, tot_ms = 0.0, 0.0
+    for c in range(16):
+        h = 2048 * c
+        plan = cpa.cpa_plan_create(db.desc, [2048], [h + 2048])
+        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+        cpa.cpa_plan_upload(plan, ws)
+        sl = slice(h, h + 2048)
+        kn, vn, sm = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl]
+        q, out = db.q[sl], db.out[sl]
+
+        def chunk():
+            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
+            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+        r = median_ms(chunk, 10, 2)
+        f = flops_chunk(64, 128, 2048, h)
+        tot_f += f
+        tot_ms += r["median_ms"]
+        rows.append({"H": h, "us": r["median_ms"] * 1e3,
+                     "tflops": f / (r["median_ms"] * 1e-3) / 1e12})
+    res = {"chunks": rows, "total_ms": tot_ms, "tflops": tot_f / (tot_ms * 1e-3) / 1e12,
+           "mfma_frac": tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    log(f"[bench] 70b-like 16x2048: {tot_ms:.2f} ms total, {res['tflops']:.1f} TFLOP/s")
+    return res
+
+
+def predictor_run(args, align=128):
+    """Startup profiling at 64 sizes (2048 down to 32, H=0) of KV write +
+    attention at the 4/4-head d=64 page-16 shape, least-squares fit, target
+    T = f(2048) - f(0), then a 32768-token prompt prefilled with predicted
+    chunks; reports measured/T per chunk."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+    b = make_batch(3, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+                   query_lens=[32768], seq_lens=[32768])
+    db = DeviceBatch(b)
+
+    def runner(L, c):
+        plan = cpa.cpa_plan_create(db.desc, [c], [L + c])
+        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+        cpa.cpa_plan_upload(plan, ws)
+        sl = slice(L, L + c)
+        kn, vn, sm, q, out = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl], db.q[sl], db.out[sl]
+
+        def f():
+            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
+            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+        return f
+
+    sizes = cpa.cpa_predictor_profile_sizes(2048, 64, 32)
+    ms = [median_ms(runner(0, l), 21, 3)["median_ms"] for l in sizes]
+    a, bb, c = cpa.cpa_predictor_fit(sizes, ms)
+    cfg = cpa.predictor_cfg(align=align)
+    T = cpa.cpa_predictor_target(cfg, a, bb)
+
+    def f_model(x):
+        return a * x * x + bb * x + c
+    chunks = []
+    L = 0
+    while L < 32768:
+        ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, 32768 - L)
+        if ch <= 0:
+            break
+        m = median_ms(runner(L, ch), 11, 2)["median_ms"]
+        model_ratio = (f_model(L + ch) - f_model(L)) / T
+        chunks.append({"L": L, "chunk": ch, "raw_x": x, "ms": m, "meas_over_T": m / T,
+                       "model_over_T": model_ratio, "meas_over_f_base": m / f_model(2048),
+                       "alignment_limited": model_ratio < 0.9})
+        L += ch
+    r = np.array([cch["meas_over_T"] for cch in chunks])
+    ok = np.array([not cch["alignment_limited"] for cch in chunks])
+    res = {"align": align, "fit": {"a": a, "b": bb, "c": c}, "T_ms": T,
+           "profile_ms": dict(zip(map(int, sizes), ms)), "num_chunks": len(chunks),
+           "meas_over_T": {"min": float(r.min()), "max": float(r.max()),
+                           "mean": float(r.mean()), "cv": float(r.std() / r.mean())},
+           "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1)),
+           "frac_within_10pct_not_alignment_limited":
+               float(np.mean(np.abs(r[ok] - 1) <= 0.1)) if ok.any() else None,
+           "chunks": chunks}
+    log(f"[bench] predictor align {align}: a={a:.3e} b={bb:.3e} c={c:.3e} T={T:.4f} ms, "
+        f"{len(chunks)} chunks, meas/T in [{r.min():.2f}, {r.max():.2f}]")
+    return res
+
+
+def cpu_baseline(budget_s=20.0):
+    """The fp64 oracle on host cores: the H=12288 Llama-3-8B chunk, query
+    heads taken one at a time until about budget_s seconds have passed."""
+    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
+    from oracle.attention import causal_chunk_attention, gather_sequence, widen_bf16
+    from oracle.kv_cache import kv_write
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpool_info()]
+        threads = max([i["threads"] or 1 for i in blas] or [1])
+    except Exception:
+        blas, threads = [], os.cpu_count()
+    h = 12288
+    b = llama3_8b_chunk(h)
+    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+    n = h + CHUNK
+    t0 = time.perf_counter()
+    k = widen_bf16(gather_sequence(kc, b.block_table[0], n, b.page_size))
+    v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size))
+    q = widen_bf16(b.q)
+    heads = 0
+    while heads < 32:
+        g = heads // 4
+        causal_chunk_attention(q[:, heads], k[:, g], v[:, g], h, 1.0 / math.sqrt(128))
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    f = flops_chunk(heads, 128, CHUNK, h)
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except Exception:
+        aff = os.cpu_count()
+    res = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"Llama-3-8B chunk C=512 at H=12288, {heads} of 32 query heads "
+                     f"(all 512 rows each), fp64 NumPy, gather included; {dt:.1f} s",
+           "seconds": dt, "cpu_count": os.cpu_count(), "affinity": aff, "blas": blas}
+    log(f"[bench] cpu oracle: {heads} heads in {dt:.1f} s -> {res['value']*1e3:.2f} GFLOP/s")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(each GPU would run its own heads or sequences with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count}")
+
+    head = headline(args)
+    out = {
+        "metric": "chunked-prefill attn TFLOP/s (% MFMA peak) at C=512, H=0..12k; decode GB/s",
+        "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3-8B attention layer (32 q / 8 kv heads, d=128), "
+                               "page 128, one 512-token chunk at each H in 0/4096/8192/12288; "
+                               "KV write + attention per chunk",
+                   "chunk": CHUNK, "hist": list(HIST_SWEEP), "page_size": 128},
+        "roofline": head["roofline"], "per_H": head["per_H"],
+    }
+    if not args.no_decode or args.extras:
+        from chunked_prefill_attention_slot_amd.inputs import mixed_llama13b
+        from chunked_prefill_attention_slot_amd.device import DeviceBatch
+        b = mixed_llama13b()
+        mixed = (b, DeviceBatch(b))
+        mixed[1].kv_write()
+        torch.cuda.synchronize()
+        if not args.no_decode:
+            out["decode"] = decode_rows(args, mixed)
+        if args.extras:
+            out["mixed_batch"] = mixed_extras(args, mixed)
+        del mixed
+        torch.cuda.empty_cache()
+    if args.extras:
+        out["long_context"] = long_context(args)
+        out["predictor"] = predictor_run(args, 128)
+        out["predictor_align16"] = predictor_run(args, 16)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    out["context_from_pages"] = {
+        "note": "whole-model figures on A100 from the vLLM chunked-prefill article, "
+                "section 2.1; not this kernel, not comparable",
+        "llama13b_2048_token_prefill_ms": 120, "decode_ms_per_token": 25}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,285 @@
+"""Thin ctypes binding of libcpa (include/cpa.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device pointers, the
+current HIP stream supplies the queue, numpy/int arrays supply host
+metadata. Every step of the computation runs in libcpa's kernels or its
+host runtime. Importing this module loads the library and raises if it has
+not been built (python -m chunked_prefill_attention_slot_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpa.so")
+
+CPA_OK = 0
+CPA_ERR_INVALID_ARG = -1
+CPA_ERR_UNSUPPORTED = -2
+CPA_ERR_WORKSPACE = -3
+CPA_ERR_HIP = -4
+CPA_ERR_NUMERIC = -5
+CPA_DTYPE_BF16 = 0
+CPA_DTYPE_F32 = 1
+
+# Every symbol include/cpa.h declares.
+EXPORTS = (
+    "cpa_last_error", "cpa_version", "cpa_kv_write", "cpa_plan_create",
+    "cpa_plan_destroy", "cpa_plan_get_info", "cpa_plan_upload",
+    "cpa_attention", "cpa_validate_metadata", "cpa_predictor_profile_sizes",
+    "cpa_predictor_fit", "cpa_predictor_target", "cpa_predictor_next_chunk",
+)
+
+
+class CpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libcpa status {status}: {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcpa is not built ({LIB_PATH} missing); run "
+                      "python -m chunked_prefill_attention_slot_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class cpa_layer_desc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("out_dtype", ctypes.c_int32)]
+
+
+class cpa_plan_options(ctypes.Structure):
+    _fields_ = [("target_items", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("prefill_split", ctypes.c_int32), ("decode_split_keys", ctypes.c_int32)]
+
+
+class cpa_plan_info(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_prefill_items", ctypes.c_int32), ("num_decode_items", ctypes.c_int32),
+                ("num_combine_items", ctypes.c_int32), ("num_partial_rows", ctypes.c_int32),
+                ("visible_pairs", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class cpa_predictor_cfg(ctypes.Structure):
+    _fields_ = [("base_chunk_size", ctypes.c_int64), ("align", ctypes.c_int64),
+                ("min_chunk", ctypes.c_int64), ("max_chunk", ctypes.c_int64),
+                ("max_model_len", ctypes.c_int64), ("smooth_factor", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_F64P = ctypes.POINTER(ctypes.c_double)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("cpa_last_error", ctypes.c_char_p)
+_sig("cpa_version", ctypes.c_char_p)
+_sig("cpa_kv_write", ctypes.c_int32, ctypes.POINTER(cpa_layer_desc), _P, _P, _P,
+     ctypes.c_int32, _P, _P, _P)
+_sig("cpa_plan_create", ctypes.c_int32, ctypes.POINTER(cpa_layer_desc), _I32P, _I32P,
+     ctypes.c_int32, ctypes.POINTER(cpa_plan_options), ctypes.POINTER(_P),
+     ctypes.POINTER(ctypes.c_size_t))
+_sig("cpa_plan_destroy", ctypes.c_int32, _P)
+_sig("cpa_plan_get_info", ctypes.c_int32, _P, ctypes.POINTER(cpa_plan_info))
+_sig("cpa_plan_upload", ctypes.c_int32, _P, _P, ctypes.c_size_t, _P)
+_sig("cpa_attention", ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P)
+_sig("cpa_validate_metadata", ctypes.c_int32, ctypes.POINTER(cpa_layer_desc), _I32P,
+     ctypes.c_int32, _I32P, _I32P, _I32P, ctypes.c_int32)
+_sig("cpa_predictor_profile_sizes", ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+     ctypes.c_int64, _I64P)
+_sig("cpa_predictor_fit", ctypes.c_int32, _F64P, _F64P, ctypes.c_int32, _F64P, _F64P, _F64P)
+_sig("cpa_predictor_target", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
+     ctypes.c_double, ctypes.c_double, _F64P)
+_sig("cpa_predictor_next_chunk", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
+     ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64, ctypes.c_int64,
+     _I64P, _F64P)
+
+
+def _check(status: int):
+    if status != CPA_OK:
+        raise CpaError(status, cpa_last_error())
+
+
+def cpa_last_error() -> str:
+    return _lib.cpa_last_error().decode()
+
+
+def cpa_version() -> str:
+    return _lib.cpa_version().decode()
+
+
+def layer_desc(num_q_heads, num_kv_heads, head_dim, page_size, num_blocks,
+               max_blocks_per_seq, scale=None, out_dtype=CPA_DTYPE_BF16) -> cpa_layer_desc:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return cpa_layer_desc(num_q_heads, num_kv_heads, head_dim, page_size, num_blocks,
+                          max_blocks_per_seq, scale, out_dtype)
+
+
+# ---- device-pointer marshalling --------------------------------------------
+
+def _dev(t, name, elem_size=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def _host_i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_I32P)
+
+
+def cpa_kv_write(desc, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+    n = int(slot_mapping.shape[0])
+    _check(_lib.cpa_kv_write(ctypes.byref(desc), _dev(k_new, "k_new", 2),
+                             _dev(v_new, "v_new", 2), _dev(slot_mapping, "slot_mapping", 4),
+                             n, _dev(k_cache, "k_cache", 2), _dev(v_cache, "v_cache", 2),
+                             _stream(stream)))
+
+
+class Plan:
+    """Owns a cpa_plan handle (destroyed with the object)."""
+
+    def __init__(self, handle, workspace_bytes, desc):
+        self._h = handle
+        self.workspace_bytes = int(workspace_bytes)
+        self.desc = desc
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        inf = cpa_plan_info()
+        _check(_lib.cpa_plan_get_info(self._h, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def destroy(self):
+        if self._h:
+            _lib.cpa_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def cpa_plan_create(desc, query_lens: Sequence[int], seq_lens: Sequence[int],
+                    options: cpa_plan_options | dict | None = None) -> Plan:
+    ql, qlp = _host_i32(query_lens)
+    sl, slp = _host_i32(seq_lens)
+    if ql.shape != sl.shape:
+        raise ValueError("query_lens and seq_lens differ in length")
+    if isinstance(options, dict):
+        options = cpa_plan_options(**options)
+    h = _P()
+    ws = ctypes.c_size_t()
+    _check(_lib.cpa_plan_create(ctypes.byref(desc), qlp, slp, int(ql.shape[0]),
+                                ctypes.byref(options) if options is not None else None,
+                                ctypes.byref(h), ctypes.byref(ws)))
+    return Plan(h, ws.value, desc)
+
+
+def cpa_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def cpa_plan_get_info(plan: Plan) -> dict:
+    return plan.info()
+
+
+def cpa_plan_upload(plan: Plan, workspace, stream=None):
+    _check(_lib.cpa_plan_upload(plan.handle, _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def cpa_attention(plan: Plan, q, k_cache, v_cache, block_table, out, workspace, stream=None):
+    _check(_lib.cpa_attention(plan.handle, _dev(q, "q", 2), _dev(k_cache, "k_cache", 2),
+                              _dev(v_cache, "v_cache", 2), _dev(block_table, "block_table", 4),
+                              _dev(out, "out"), _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def cpa_validate_metadata(desc, slot_mapping=None, block_table=None, query_lens=None,
+                          seq_lens=None) -> None:
+    def opt(a):
+        if a is None:
+            return None, None
+        return _host_i32(a)
+    sm, smp = opt(slot_mapping)
+    bt, btp = opt(None if block_table is None else np.asarray(block_table).reshape(-1))
+    ql, qlp = opt(query_lens)
+    sl, slp = opt(seq_lens)
+    _check(_lib.cpa_validate_metadata(ctypes.byref(desc), smp,
+                                      0 if sm is None else int(sm.shape[0]), btp, qlp, slp,
+                                      0 if ql is None else int(ql.shape[0])))
+
+
+# ---- predictor (host only) -----------------------------------------------
+
+def predictor_cfg(base_chunk_size=2048, align=128, min_chunk=64, max_chunk=2048,
+                  max_model_len=32768, smooth_factor=1.0) -> cpa_predictor_cfg:
+    return cpa_predictor_cfg(base_chunk_size, align, min_chunk, max_chunk, max_model_len,
+                             smooth_factor)
+
+
+def cpa_predictor_profile_sizes(base: int, n: int, lo: int) -> list[int]:
+    out = (ctypes.c_int64 * n)()
+    _check(_lib.cpa_predictor_profile_sizes(base, n, lo, out))
+    return list(out)
+
+
+def cpa_predictor_fit(lens, ms):
+    l = np.ascontiguousarray(lens, dtype=np.float64)
+    t = np.ascontiguousarray(ms, dtype=np.float64)
+    a, b, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(_lib.cpa_predictor_fit(l.ctypes.data_as(_F64P), t.ctypes.data_as(_F64P),
+                                  int(l.shape[0]), ctypes.byref(a), ctypes.byref(b),
+                                  ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def cpa_predictor_target(cfg, a: float, b: float) -> float:
+    T = ctypes.c_double()
+    _check(_lib.cpa_predictor_target(ctypes.byref(cfg), a, b, ctypes.byref(T)))
+    return T.value
+
+
+def cpa_predictor_next_chunk(cfg, a: float, b: float, T: float, history_len: int,
+                             remaining: int):
+    chunk = ctypes.c_int64()
+    x = ctypes.c_double()
+    _check(_lib.cpa_predictor_next_chunk(ctypes.byref(cfg), a, b, T, int(history_len),
+                                         int(remaining), ctypes.byref(chunk), ctypes.byref(x)))
+    return chunk.value, x.value

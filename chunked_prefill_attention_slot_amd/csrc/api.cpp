@@ -1,0 +1,443 @@
+// C ABI entry points of libcpa, and the host-side attention planner.
+//
+// The planner turns the per-sequence metadata of a flattened batch (the
+// Ascend dual-stream article, section 3.1: query_lens and seq_lens per
+// sequence, tokens concatenated on one axis, seq_len = prefix + current)
+// into lists of work items for the kernels:
+//   * prefill chunks (query_len >= 2): one item per (sequence, KV head,
+//     head sub-group, 128-row query tile), the key range split into pieces
+//     when there are too few tiles to fill the GPU; split tiles also get a
+//     combine item;
+//   * decode rows (query_len == 1): one item per (sequence, KV head, key
+//     range of decode_split_keys), merged by a combine item when split.
+// Items are ordered longest key range first so the tail of the grid holds
+// the short ones.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "cpa.h"
+#include "cpa_host.h"
+#include "cpa_internal.h"
+
+namespace cpa {
+
+std::string& last_error() {
+  thread_local std::string msg;
+  return msg;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kDefaultCus = 256;
+constexpr int kMinSplitKeys = 1024;
+constexpr int kDefaultDecodeSplit = 512;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+cpa_status hip_fail(hipError_t e, const char* what) {
+  return fail(CPA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return ((1 << l) == v) ? l : -1;
+}
+
+cpa_status check_desc(const cpa_layer_desc* d) {
+  if (!d) return fail(CPA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+    return fail(CPA_ERR_INVALID_ARG, "need num_q_heads > 0, num_kv_heads > 0, Hq % Hkv == 0");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(CPA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int pl = log2_exact(d->page_size);
+  if (d->page_size < 16 || d->page_size > 1024 || pl < 0)
+    return fail(CPA_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 1024]");
+  if (d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
+    return fail(CPA_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be > 0");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale))
+    return fail(CPA_ERR_NUMERIC, "scale must be finite and > 0");
+  if (d->out_dtype != CPA_DTYPE_BF16 && d->out_dtype != CPA_DTYPE_F32)
+    return fail(CPA_ERR_INVALID_ARG, "out_dtype must be CPA_DTYPE_BF16 or CPA_DTYPE_F32");
+  if ((int64_t)d->num_blocks * d->page_size >= (int64_t)1 << 31)
+    return fail(CPA_ERR_UNSUPPORTED, "num_blocks * page_size must be < 2^31 slots");
+  return CPA_OK;
+}
+
+cpa_status check_lens(const cpa_layer_desc* d, const int32_t* ql, const int32_t* sl, int32_t S,
+                      int64_t* total_tokens) {
+  if (S < 0) return fail(CPA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (S > 0 && (!ql || !sl)) return fail(CPA_ERR_INVALID_ARG, "query_lens/seq_lens is NULL");
+  int64_t total = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    if (ql[s] < 0 || ql[s] > sl[s])
+      return fail(CPA_ERR_INVALID_ARG, "sequence " + std::to_string(s) +
+                                           ": need 0 <= query_len <= seq_len");
+    const int64_t pages = ((int64_t)sl[s] + d->page_size - 1) / d->page_size;
+    if (pages > d->max_blocks_per_seq)
+      return fail(CPA_ERR_INVALID_ARG, "sequence " + std::to_string(s) +
+                                           ": ceil(seq_len/page_size) > max_blocks_per_seq");
+    total += ql[s];
+  }
+  if (total >= ((int64_t)1 << 31) / std::max(1, d->num_q_heads))
+    return fail(CPA_ERR_UNSUPPORTED, "too many tokens for 32-bit row indices");
+  *total_tokens = total;
+  return CPA_OK;
+}
+
+// Which plan currently owns which workspace.
+std::mutex g_ws_mu;
+std::unordered_map<const void*, uint64_t> g_ws_owner;
+uint64_t g_next_plan_id = 1;
+
+}  // namespace
+}  // namespace cpa
+
+struct cpa_plan_s {
+  cpa_layer_desc desc;
+  int32_t num_seqs = 0, num_tokens = 0;
+  int32_t group = 1;             // Hq / Hkv
+  int32_t decode_group = 0;      // heads per decode item, 0 if no decode kernel
+  int32_t part_rows = 0, max_combine_rows = 0;
+  int64_t visible_pairs = 0;
+  std::vector<cpa::WorkItem> prefill, decode;
+  std::vector<cpa::CombineItem> combine;
+  size_t off_prefill = 0, off_decode = 0, off_combine = 0, off_part_o = 0, off_part_ml = 0;
+  size_t ws_bytes = 0;
+  uint64_t id = 0;
+  std::vector<uint8_t> image;    // host copy of the work lists, uploaded as is
+};
+
+namespace {
+
+struct Tile {
+  int32_t seq, kvh, head0, nheads, tok0, q0, nq, hist, kv_len;
+};
+
+void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, int nsplit,
+               int align) {
+  cpa::WorkItem base{t.seq, t.kvh, t.head0, t.nheads, t.tok0, t.q0, t.nq, t.hist, 0, t.kv_len, -1, 0};
+  if (nsplit <= 1 || t.kv_len <= align) {
+    out.push_back(base);
+    return;
+  }
+  const int per = (int)cpa::round_up((size_t)((t.kv_len + nsplit - 1) / nsplit), (size_t)align);
+  nsplit = (t.kv_len + per - 1) / per;
+  if (nsplit <= 1) {
+    out.push_back(base);
+    return;
+  }
+  const int rows = t.nq * t.nheads;
+  const int part0 = p->part_rows;
+  p->part_rows += nsplit * rows;
+  p->max_combine_rows = std::max(p->max_combine_rows, rows);
+  p->combine.push_back(cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, nsplit, part0, rows, 0});
+  for (int k = 0; k < nsplit; ++k) {
+    cpa::WorkItem w = base;
+    w.kv0 = k * per;
+    w.kv1 = std::min(t.kv_len, (k + 1) * per);
+    w.part = part0 + k * rows;
+    out.push_back(w);
+  }
+}
+
+void order_longest_first(std::vector<cpa::WorkItem>& v) {
+  std::stable_sort(v.begin(), v.end(), [](const cpa::WorkItem& x, const cpa::WorkItem& y) {
+    return (x.kv1 - x.kv0) > (y.kv1 - y.kv0);
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cpa_last_error(void) { return cpa::last_error().c_str(); }
+
+const char* cpa_version(void) { return "cpa 0.1.0 (gfx950)"; }
+
+cpa_status cpa_kv_write(const cpa_layer_desc* desc, const void* k_new, const void* v_new,
+                        const int32_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                        void* v_cache, hipStream_t stream) {
+  cpa_status st = cpa::check_desc(desc);
+  if (st != CPA_OK) return st;
+  if (num_tokens < 0) return cpa::fail(CPA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_tokens == 0) return cpa::ok();
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "kv_write: NULL pointer");
+  const hipError_t e = cpa::launch_kv_write(
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+      num_tokens, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+      desc->num_kv_heads, desc->head_dim, cpa::log2_exact(desc->page_size), desc->num_blocks,
+      stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "kv_write launch");
+  return cpa::ok();
+}
+
+cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens,
+                           const int32_t* seq_lens, int32_t num_seqs,
+                           const cpa_plan_options* options, cpa_plan* out_plan,
+                           size_t* workspace_bytes) {
+  if (!out_plan || !workspace_bytes)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "plan_create: NULL output pointer");
+  *out_plan = nullptr;
+  cpa_status st = cpa::check_desc(desc);
+  if (st != CPA_OK) return st;
+  int64_t total = 0;
+  st = cpa::check_lens(desc, query_lens, seq_lens, num_seqs, &total);
+  if (st != CPA_OK) return st;
+  cpa_plan_options opt{};
+  if (options) opt = *options;
+  if (opt.target_items < 0 || opt.num_cus < 0 || opt.prefill_split < 0 ||
+      opt.decode_split_keys < 0)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "plan options must be >= 0");
+
+  cpa_plan_s* p = new (std::nothrow) cpa_plan_s();
+  if (!p) return cpa::fail(CPA_ERR_INVALID_ARG, "plan_create: out of host memory");
+  p->desc = *desc;
+  p->num_seqs = num_seqs;
+  p->num_tokens = (int32_t)total;
+  const int Hq = desc->num_q_heads, Hkv = desc->num_kv_heads;
+  const int G = Hq / Hkv;
+  p->group = G;
+  // Heads packed per prefill tile: the largest power of two dividing G (it
+  // divides the 128 rows); the tile then holds 128/GP queries.
+  int GP = 1;
+  while (GP < cpa::kPrefillRows && G % (GP * 2) == 0) GP *= 2;
+  const int QT = cpa::kPrefillRows / GP;
+  const bool decode_kernel = cpa::decode_group_supported(G);
+  p->decode_group = decode_kernel ? G : 0;
+
+  std::vector<Tile> tiles;
+  std::vector<int32_t> decode_seqs;
+  int32_t tok = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ql = query_lens[s], n = seq_lens[s], hist = n - ql;
+    p->visible_pairs += (int64_t)Hq * ((int64_t)ql * hist + (int64_t)ql * (ql + 1) / 2);
+    if (ql == 1 && decode_kernel) {
+      decode_seqs.push_back(s);
+    } else if (ql > 0) {
+      for (int g = 0; g < Hkv; ++g)
+        for (int hs = 0; hs < G / GP; ++hs)
+          for (int q0 = 0; q0 < ql; q0 += QT) {
+            const int nq = std::min(QT, ql - q0);
+            tiles.push_back(Tile{s, g, g * G + hs * GP, GP, tok + q0, q0, nq, hist, hist + q0 + nq});
+          }
+    }
+    tok += ql;
+  }
+
+  // Split long prefill key ranges when the tiles alone cannot fill the GPU.
+  const int cus = opt.num_cus > 0 ? opt.num_cus : cpa::kDefaultCus;
+  const int target = opt.target_items > 0 ? opt.target_items : 2 * cus;
+  int64_t total_keys = 0;
+  for (const Tile& t : tiles) total_keys += t.kv_len;
+  int64_t chunk_keys = INT64_MAX;
+  if (opt.prefill_split == 0 && (int64_t)tiles.size() < target && !tiles.empty()) {
+    chunk_keys = (int64_t)cpa::round_up((size_t)((total_keys + target - 1) / target),
+                                        cpa::kSplitAlign);
+    chunk_keys = std::max<int64_t>(chunk_keys, cpa::kMinSplitKeys);
+  }
+  for (const Tile& t : tiles) {
+    int nsplit = 1;
+    if (opt.prefill_split > 0)
+      nsplit = opt.prefill_split;
+    else if (chunk_keys != INT64_MAX)
+      nsplit = (int)((t.kv_len + chunk_keys - 1) / chunk_keys);
+    add_split(p, p->prefill, t, nsplit, cpa::kSplitAlign);
+  }
+
+  const int dsk = opt.decode_split_keys > 0 ? opt.decode_split_keys : cpa::kDefaultDecodeSplit;
+  std::vector<int32_t> qsl((size_t)num_seqs + 1, 0);
+  for (int32_t s = 0; s < num_seqs; ++s) qsl[s + 1] = qsl[s] + query_lens[s];
+  for (int32_t s : decode_seqs) {
+    const int32_t t0 = qsl[s];
+    const int32_t n = seq_lens[s];
+    for (int g = 0; g < Hkv; ++g) {
+      Tile t{s, g, g * G, G, t0, 0, 1, n - 1, n};
+      add_split(p, p->decode, t, (n + dsk - 1) / dsk, 1);
+    }
+  }
+  order_longest_first(p->prefill);
+  order_longest_first(p->decode);
+
+  // Workspace: [prefill items][decode items][combine items][partial O][partial m,l]
+  size_t off = 0;
+  p->off_prefill = off;
+  off = cpa::round_up(off + p->prefill.size() * sizeof(cpa::WorkItem), cpa::kAlign);
+  p->off_decode = off;
+  off = cpa::round_up(off + p->decode.size() * sizeof(cpa::WorkItem), cpa::kAlign);
+  p->off_combine = off;
+  off = cpa::round_up(off + p->combine.size() * sizeof(cpa::CombineItem), cpa::kAlign);
+  p->off_part_o = off;
+  off = cpa::round_up(off + (size_t)p->part_rows * desc->head_dim * sizeof(float), cpa::kAlign);
+  p->off_part_ml = off;
+  off = cpa::round_up(off + (size_t)p->part_rows * 2 * sizeof(float), cpa::kAlign);
+  p->ws_bytes = std::max(off, cpa::kAlign);
+
+  p->image.assign(p->off_part_o, 0);
+  if (!p->prefill.empty())
+    std::memcpy(p->image.data() + p->off_prefill, p->prefill.data(),
+                p->prefill.size() * sizeof(cpa::WorkItem));
+  if (!p->decode.empty())
+    std::memcpy(p->image.data() + p->off_decode, p->decode.data(),
+                p->decode.size() * sizeof(cpa::WorkItem));
+  if (!p->combine.empty())
+    std::memcpy(p->image.data() + p->off_combine, p->combine.data(),
+                p->combine.size() * sizeof(cpa::CombineItem));
+  {
+    std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
+    p->id = cpa::g_next_plan_id++;
+  }
+  *out_plan = p;
+  *workspace_bytes = p->ws_bytes;
+  return cpa::ok();
+}
+
+cpa_status cpa_plan_destroy(cpa_plan plan) {
+  if (!plan) return cpa::ok();
+  {
+    std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
+    for (auto it = cpa::g_ws_owner.begin(); it != cpa::g_ws_owner.end();) {
+      if (it->second == plan->id)
+        it = cpa::g_ws_owner.erase(it);
+      else
+        ++it;
+    }
+  }
+  delete plan;
+  return cpa::ok();
+}
+
+cpa_status cpa_plan_get_info(cpa_plan plan, cpa_plan_info* info) {
+  if (!plan || !info) return cpa::fail(CPA_ERR_INVALID_ARG, "plan_get_info: NULL pointer");
+  info->num_seqs = plan->num_seqs;
+  info->num_tokens = plan->num_tokens;
+  info->num_prefill_items = (int32_t)plan->prefill.size();
+  info->num_decode_items = (int32_t)plan->decode.size();
+  info->num_combine_items = (int32_t)plan->combine.size();
+  info->num_partial_rows = plan->part_rows;
+  info->visible_pairs = plan->visible_pairs;
+  info->workspace_bytes = plan->ws_bytes;
+  return cpa::ok();
+}
+
+cpa_status cpa_plan_upload(cpa_plan plan, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!plan || !workspace) return cpa::fail(CPA_ERR_INVALID_ARG, "plan_upload: NULL pointer");
+  if (workspace_bytes < plan->ws_bytes)
+    return cpa::fail(CPA_ERR_WORKSPACE, "plan_upload: workspace has " +
+                                            std::to_string(workspace_bytes) + " bytes, plan needs " +
+                                            std::to_string(plan->ws_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % cpa::kAlign != 0)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "plan_upload: workspace must be 256-byte aligned");
+  if (!plan->image.empty()) {
+    const hipError_t e = hipMemcpyAsync(workspace, plan->image.data(), plan->image.size(),
+                                        hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return cpa::hip_fail(e, "plan_upload copy");
+  }
+  std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
+  cpa::g_ws_owner[workspace] = plan->id;
+  return cpa::ok();
+}
+
+cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!plan) return cpa::fail(CPA_ERR_INVALID_ARG, "attention: plan is NULL");
+  if (plan->num_tokens == 0) return cpa::ok();
+  if (!q || !k_cache || !v_cache || !block_table || !out || !workspace)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "attention: NULL pointer");
+  if (workspace_bytes < plan->ws_bytes)
+    return cpa::fail(CPA_ERR_WORKSPACE, "attention: workspace smaller than the plan needs");
+  {
+    std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
+    auto it = cpa::g_ws_owner.find(workspace);
+    if (it == cpa::g_ws_owner.end() || it->second != plan->id)
+      return cpa::fail(CPA_ERR_WORKSPACE,
+                       "attention: this plan was not uploaded to this workspace "
+                       "(call cpa_plan_upload first)");
+  }
+  const cpa_layer_desc& d = plan->desc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  cpa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.bt_stride = d.max_blocks_per_seq;
+  a.num_q_heads = d.num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.page_log2 = cpa::log2_exact(d.page_size);
+  a.num_blocks = d.num_blocks;
+  a.scale_log2e = d.scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
+  a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
+
+  hipError_t e = cpa::launch_prefill(
+      reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_prefill), (int)plan->prefill.size(), a,
+      d.head_dim, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "prefill attention launch");
+  e = cpa::launch_decode(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_decode),
+                         (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "decode attention launch");
+  e = cpa::launch_combine(reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine),
+                          (int)plan->combine.size(), plan->max_combine_rows, a, d.head_dim, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
+  return cpa::ok();
+}
+
+cpa_status cpa_validate_metadata(const cpa_layer_desc* desc, const int32_t* slot_mapping,
+                                 int32_t num_tokens, const int32_t* block_table,
+                                 const int32_t* query_lens, const int32_t* seq_lens,
+                                 int32_t num_seqs) {
+  cpa_status st = cpa::check_desc(desc);
+  if (st != CPA_OK) return st;
+  const int64_t slots = (int64_t)desc->num_blocks * desc->page_size;
+  if (slot_mapping) {
+    if (num_tokens < 0) return cpa::fail(CPA_ERR_INVALID_ARG, "num_tokens < 0");
+    std::vector<uint8_t> seen((size_t)slots, 0);
+    for (int32_t t = 0; t < num_tokens; ++t) {
+      const int32_t sl = slot_mapping[t];
+      if (sl < 0) continue;
+      if (sl >= slots)
+        return cpa::fail(CPA_ERR_INVALID_ARG, "slot_mapping[" + std::to_string(t) + "] = " +
+                                                  std::to_string(sl) + " is outside the cache");
+      if (seen[(size_t)sl]++)
+        return cpa::fail(CPA_ERR_INVALID_ARG,
+                         "slot_mapping[" + std::to_string(t) + "] repeats slot " + std::to_string(sl));
+    }
+  }
+  if (query_lens && seq_lens) {
+    int64_t total = 0;
+    st = cpa::check_lens(desc, query_lens, seq_lens, num_seqs, &total);
+    if (st != CPA_OK) return st;
+    if (slot_mapping && total != num_tokens)
+      return cpa::fail(CPA_ERR_INVALID_ARG, "sum(query_lens) != num_tokens");
+    if (block_table) {
+      for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t pages = ((int64_t)seq_lens[s] + desc->page_size - 1) / desc->page_size;
+        for (int64_t j = 0; j < pages; ++j) {
+          const int32_t pg = block_table[(size_t)s * desc->max_blocks_per_seq + j];
+          if (pg < 0 || pg >= desc->num_blocks)
+            return cpa::fail(CPA_ERR_INVALID_ARG, "block_table[" + std::to_string(s) + "][" +
+                                                      std::to_string(j) + "] = " +
+                                                      std::to_string(pg) + " is outside the cache");
+        }
+      }
+    }
+  }
+  return cpa::ok();
+}
+
+}  // extern "C"

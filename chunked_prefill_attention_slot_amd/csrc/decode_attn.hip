@@ -1,0 +1,290 @@
+// Decode rows (query_len = 1) and the split-KV combine.
+//
+// A decode row is the same attention as a prefill row (vLLM
+// "Chunked-Prefills" article, section 3.2.1, one query; Ascend dual-stream
+// article, section 3.1: query_len 1, seq_len = prefix + 1), but it reads
+// every key and value once for a handful of query heads, so it is bound by
+// HBM, not by matrix throughput. This kernel therefore uses plain fp32
+// vector arithmetic and spends its effort on the memory stream:
+//   * a work item is (sequence, KV head, key range); all G query heads of
+//     the GQA group are computed from one read of each K/V row;
+//   * d/8 lanes share one key, each loading a 16-byte chunk, so a wave
+//     reads whole 256-byte rows (d = 128) out of a page;
+//   * each thread keeps U keys' K and V loads in flight before using them;
+//   * partial (max, sum, O) of the 16 key slots are merged in registers and
+//     LDS; long rows are split over several items and merged by
+//     combine_kernel (log-sum-exp weights).
+#include <math.h>
+
+#include "cpa_internal.h"
+
+namespace cpa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Merge (m2, l2, o2) into (m, l, o); m in log2 units, -inf = empty.
+template <int N>
+__device__ __forceinline__ void lse_merge(float& m, float& l, float* o, float m2, float l2,
+                                          const float* o2) {
+  const float mm = fmaxf(m, m2);
+  const float a1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+  const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mm);
+  l = l * a1 + l2 * a2;
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  m = mm;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict__ items,
+                                                     AttnArgs a) {
+  constexpr int LPK = D / 8;      // lanes per key
+  constexpr int KPW = 64 / LPK;   // keys per wave step
+  constexpr int KPB = 4 * KPW;    // keys per block step
+  constexpr int U = (G >= 8) ? 4 : 8;  // block steps loaded before use
+  __shared__ float s_m[4][G], s_l[4][G];
+  __shared__ __attribute__((aligned(16))) float s_o[4][G][D];
+
+  const WorkItem it = items[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane % LPK, ks = lane / LPK;
+  const float sl2e = a.scale_log2e;
+
+  float qv[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const u32x4 q4 = *reinterpret_cast<const u32x4*>(
+        a.q + ((size_t)it.tok0 * a.num_q_heads + it.head0 + g) * D + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qv[g][2 * j] = bf16_lo(q4[j]);
+      qv[g][2 * j + 1] = bf16_hi(q4[j]);
+    }
+  }
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+  }
+
+  const int32_t* bt = a.block_table + (size_t)it.seq * a.bt_stride;
+  const int plog = a.page_log2, pmask = (1 << plog) - 1;
+  const size_t head_off = (size_t)it.kvh << plog;
+
+  for (int base = it.kv0; base < it.kv1; base += U * KPB) {
+    u32x4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPB + w * KPW + ks;
+      ok[u] = key < it.kv1;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (ok[u]) {
+        const int page = bt[key >> plog];
+        if ((unsigned)page < (unsigned)a.num_blocks) {
+          const size_t off =
+              (((size_t)page * a.num_kv_heads << plog) + head_off + (key & pmask)) * D + 8 * c;
+          kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_cache + off));
+          vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_cache + off));
+        }
+      }
+      kr[u] = kv;
+      vr[u] = vv;
+    }
+
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kf[2 * j] = bf16_lo(kr[u][j]);
+        kf[2 * j + 1] = bf16_hi(kr[u][j]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(qv[g][e], kf[e], acc);
+#pragma unroll
+        for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
+        s[u][g] = ok[u] ? acc * sl2e : -INFINITY;
+      }
+    }
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
+      const float msc = (mx == -INFINITY) ? 0.f : mx;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - msc);
+      float psum = 0.f;
+      float p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = __builtin_amdgcn_exp2f(s[u][g] - msc);
+        psum += p[u];
+      }
+      l[g] = fmaf(l[g], alpha, psum);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = o[g][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t wv = vr[u][e >> 1];
+          acc = fmaf(p[u], (e & 1) ? bf16_hi(wv) : bf16_lo(wv), acc);
+        }
+        o[g][e] = acc;
+      }
+      m[g] = mx;
+    }
+  }
+
+  // Merge the KPW key slots of the wave (lanes with equal c).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[g][e], off);
+      const float m2 = __shfl_xor(m[g], off);
+      const float l2 = __shfl_xor(l[g], off);
+      lse_merge<8>(m[g], l[g], o[g], m2, l2, o2);
+    }
+  }
+  if (ks == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[w][g][8 * c + e] = o[g][e];
+      if (c == 0) {
+        s_m[w][g] = m[g];
+        s_l[w][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the four waves: thread -> (head g, 4 consecutive d).
+  constexpr int D4 = D / 4;
+  if (tid < G * D4) {
+    const int g = tid / D4, d = 4 * (tid % D4);
+    float mm = -INFINITY, ll = 0.f, oo[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float o2[4] = {s_o[ww][g][d], s_o[ww][g][d + 1], s_o[ww][g][d + 2],
+                           s_o[ww][g][d + 3]};
+      lse_merge<4>(mm, ll, oo, s_m[ww][g], s_l[ww][g], o2);
+    }
+    if (it.part < 0) {
+      const float inv = 1.f / ll;
+      const size_t ob = ((size_t)it.tok0 * a.num_q_heads + it.head0 + g) * D + d;
+      if (a.out_f32) {
+        f32x4 o4 = {oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob) = o4;
+      } else {
+        u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = o2;
+      }
+    } else {
+      const size_t prow = (size_t)it.part + g;
+      f32x4 o4 = {oo[0], oo[1], oo[2], oo[3]};
+      *reinterpret_cast<f32x4*>(a.part_o + prow * D + d) = o4;
+      if (d == 0) {
+        a.part_ml[prow * 2 + 0] = mm;
+        a.part_ml[prow * 2 + 1] = ll;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the split partials of one tile: thread -> (packed
+// row r, 4 consecutive d).
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
+                                                      AttnArgs a) {
+  constexpr int D4 = D / 4;
+  const CombineItem it = items[blockIdx.x];
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  const int r = idx / D4, d = 4 * (idx % D4);
+  if (r >= it.rows) return;
+  float mm = -INFINITY;
+  for (int k = 0; k < it.nsplit; ++k)
+    mm = fmaxf(mm, a.part_ml[((size_t)it.part0 + (size_t)k * it.rows + r) * 2]);
+  float ll = 0.f;
+  f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < it.nsplit; ++k) {
+    const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
+    const float mk = a.part_ml[prow * 2];
+    const float wk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - mm);
+    ll = fmaf(wk, a.part_ml[prow * 2 + 1], ll);
+    const f32x4 ok = *reinterpret_cast<const f32x4*>(a.part_o + prow * D + d);
+    oo += wk * ok;
+  }
+  const float inv = 1.f / ll;
+  const int qi = r / it.nheads, hl = r - qi * it.nheads;
+  const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D + d;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob) = oo * inv;
+  } else {
+    u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = o2;
+  }
+}
+
+template <int D>
+hipError_t launch_decode_d(const WorkItem* items, int n, const AttnArgs& a, int group,
+                           hipStream_t s) {
+  switch (group) {
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(n), dim3(256), 0, s, items, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(n), dim3(256), 0, s, items, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), dim3(n), dim3(256), 0, s, items, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8>), dim3(n), dim3(256), 0, s, items, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const WorkItem* items, int num_items, const AttnArgs& a, int head_dim,
+                         int group, hipStream_t stream) {
+  if (num_items == 0) return hipSuccess;
+  if (head_dim == 128) return launch_decode_d<128>(items, num_items, a, group, stream);
+  if (head_dim == 64) return launch_decode_d<64>(items, num_items, a, group, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows,
+                          const AttnArgs& a, int head_dim, hipStream_t stream) {
+  if (num_items == 0) return hipSuccess;
+  const int threads = max_rows * (head_dim / 4);
+  const dim3 grid(num_items, (threads + 255) / 256);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, items, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, items, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace cpa

@@ -1,0 +1,261 @@
+/*
+ * cpa.h -- C ABI of libcpa: paged chunked-prefill attention on gfx950.
+ *
+ * The library computes, on one AMD Instinct MI355X (gfx950), the attention
+ * step of chunked prefill: a chunk of C new query tokens of a sequence
+ * attends causally to the H tokens already in its paged KV cache plus
+ * itself; decode rows (one query token) share the same call. It also holds
+ * the host-side chunk-size predictor that sizes those chunks.
+ *
+ * Sources (cited by page title and section):
+ *   [CPP]  vllm-ascend design document "Dynamic chunked pipeline parallel
+ *          (CPP)": quadratic latency model, startup profiling, runtime
+ *          prediction (solve f(L+x)-f(L)=T, smooth, align, cap), online
+ *          calibration.
+ *   [CP]   "vLLM Chunked-Prefills" article: section 3.1 (chunks cache their
+ *          KV; token budget), section 3.2.1 (chunked attention over
+ *          concatenated cached + new K/V), section 2.2.3 (a flattened
+ *          token axis for batched tokens).
+ *   [DS]   Ascend "dual-stream parallel for Qwen3 dense" article,
+ *          section 3.1: attn_metadata fields num_actual_tokens,
+ *          slot_mapping [bs], seq_lens [batch] (prefix + current tokens),
+ *          query_lens [batch], block_table [batch, num_blocks].
+ *
+ * Conventions for every entry point:
+ *   - Return a cpa_status; CPA_OK is 0, errors are negative. On error,
+ *     cpa_last_error() returns a message for the calling thread. No C++
+ *     exception crosses this boundary.
+ *   - Device pointers are owned by the caller, must stay valid until the
+ *     work queued on `stream` has finished, and are never freed here. The
+ *     library allocates no device memory; host memory it allocates belongs
+ *     to a plan and is released by cpa_plan_destroy.
+ *   - GPU work is queued on `stream` (a hipStream_t; 0 = the null stream)
+ *     and is asynchronous to the host. Host arrays are read during the call
+ *     only.
+ *   - bf16 tensors are raw 16-bit bfloat16 bit patterns, row-major,
+ *     contiguous, 16-byte aligned.
+ *   - Contents of device index arrays (slot_mapping, block_table) are
+ *     trusted for speed; kernels skip slots and pages outside the cache
+ *     instead of faulting. cpa_validate_metadata checks them on the host.
+ */
+#ifndef CPA_H_
+#define CPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t cpa_status;
+#define CPA_OK 0
+#define CPA_ERR_INVALID_ARG (-1) /* bad pointer, size, or metadata */
+#define CPA_ERR_UNSUPPORTED (-2) /* valid but not implemented (e.g. head_dim) */
+#define CPA_ERR_WORKSPACE (-3)   /* workspace too small, or holds another plan */
+#define CPA_ERR_HIP (-4)         /* a HIP runtime call or launch failed */
+#define CPA_ERR_NUMERIC (-5)     /* non-finite or degenerate numeric input */
+
+#define CPA_DTYPE_BF16 0
+#define CPA_DTYPE_F32 1
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* cpa_last_error(void);
+/* Library version string. */
+const char* cpa_version(void);
+
+/*
+ * One attention layer's shape.
+ *   num_q_heads, num_kv_heads: Hq and Hkv, Hq % Hkv == 0; query head h
+ *     reads KV head h / (Hq/Hkv) (contiguous groups).
+ *   head_dim: d, 64 or 128.
+ *   page_size: P tokens per cache page, a power of two, 16..1024.
+ *   num_blocks: NB physical pages in each cache buffer.
+ *   max_blocks_per_seq: row stride of block_table.
+ *   scale: softmax scale applied to Q.K (normally 1/sqrt(d)).
+ *   out_dtype: CPA_DTYPE_BF16 or CPA_DTYPE_F32 for the attention output.
+ * Cache layout ([DS] section 3.1 leaves it open): K and V are separate
+ * buffers of [NB, Hkv, P, d] bf16; slot s is page s / P, offset s % P.
+ */
+typedef struct cpa_layer_desc {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  float scale;
+  int32_t out_dtype;
+} cpa_layer_desc;
+
+/*
+ * KV write ([DS] section 3.1, slot_mapping; [CP] section 3.1, each chunk
+ * caches its KV). For every token t < num_tokens with slot_mapping[t] >= 0:
+ *   k_cache[slot/P, h, slot%P, :] = k_new[t, h, :]   for h < Hkv
+ * and the same for v. Slots < 0 are skipped (padding); slots >= NB*P are
+ * skipped. Duplicate slots within one call give an unspecified winner.
+ *   k_new, v_new: device [num_tokens, Hkv, d] bf16.
+ *   slot_mapping: device [num_tokens] int32.
+ *   k_cache, v_cache: device [NB, Hkv, P, d] bf16, written in place.
+ * num_tokens == 0 queues nothing and returns CPA_OK.
+ */
+cpa_status cpa_kv_write(const cpa_layer_desc* desc, const void* k_new,
+                        const void* v_new, const int32_t* slot_mapping,
+                        int32_t num_tokens, void* k_cache, void* v_cache,
+                        hipStream_t stream);
+
+/*
+ * Attention plan. Built on the host from host copies of query_lens and
+ * seq_lens ([DS] section 3.1); it splits the flattened batch into work
+ * items (sequence, KV head, query tile, key range) and sizes the device
+ * workspace. A plan is immutable and may serve any number of layers that
+ * share the same metadata (same desc shape and lengths).
+ */
+typedef struct cpa_plan_s* cpa_plan;
+
+/* Tuning knobs; zero selects the default for a field. */
+typedef struct cpa_plan_options {
+  int32_t target_items;     /* work items to aim for (default 2 x CUs) */
+  int32_t num_cus;          /* compute units to plan for (default 256) */
+  int32_t prefill_split;    /* force this many key splits per prefill
+                               tile (default: chosen from the work) */
+  int32_t decode_split_keys;/* keys per decode split (default 512) */
+} cpa_plan_options;
+
+/*
+ * Builds a plan for num_seqs sequences. Sequence s contributes
+ * query_lens[s] tokens to the flat token axis (in order s = 0, 1, ...) at
+ * absolute positions seq_lens[s]-query_lens[s] .. seq_lens[s]-1; it sees
+ * its prefix of H = seq_lens[s]-query_lens[s] cached tokens plus itself,
+ * causally. Rows with query_len == 1 are decode rows; others are prefill
+ * chunks; query_len == 0 contributes nothing.
+ * Validates: 0 <= query_len <= seq_len, ceil(seq_len/P) <=
+ * max_blocks_per_seq, head_dim in {64, 128}, Hq % Hkv == 0, page_size a
+ * power of two in 16..1024, total tokens < 2^31.
+ *   options may be NULL. *workspace_bytes receives the device workspace
+ *   size cpa_attention needs. On error *out_plan is NULL.
+ */
+cpa_status cpa_plan_create(const cpa_layer_desc* desc,
+                           const int32_t* query_lens, const int32_t* seq_lens,
+                           int32_t num_seqs, const cpa_plan_options* options,
+                           cpa_plan* out_plan, size_t* workspace_bytes);
+
+cpa_status cpa_plan_destroy(cpa_plan plan);
+
+typedef struct cpa_plan_info {
+  int32_t num_seqs;
+  int32_t num_tokens;          /* sum of query_lens */
+  int32_t num_prefill_items;   /* work items of the MFMA kernel */
+  int32_t num_decode_items;    /* work items of the decode kernel */
+  int32_t num_combine_items;   /* tiles whose key range was split */
+  int32_t num_partial_rows;    /* fp32 partial rows in the workspace */
+  int64_t visible_pairs;       /* sum over rows and q heads of keys seen */
+  size_t workspace_bytes;
+} cpa_plan_info;
+
+cpa_status cpa_plan_get_info(cpa_plan plan, cpa_plan_info* info);
+
+/*
+ * Copies the plan's work lists into `workspace` (device, at least
+ * workspace_bytes as returned by cpa_plan_create, 256-byte aligned), queued
+ * on `stream`. A workspace holds one plan at a time: uploading another plan
+ * into the same workspace replaces it, and cpa_attention then refuses the
+ * first plan with CPA_ERR_WORKSPACE.
+ */
+cpa_status cpa_plan_upload(cpa_plan plan, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunked-prefill / decode attention over the plan's flattened batch
+ * ([CP] section 3.2.1 with a causal mask offset by the prefix; [DS]
+ * section 3.1 metadata). For every sequence s, query row i < query_len[s]
+ * (flat token t = sum(query_lens[:s]) + i, absolute position p = H_s + i)
+ * and query head h (KV head g = h / (Hq/Hkv)):
+ *   out[t, h, :] = sum_{j <= p} softmax_j(scale * q[t,h,:].K_j) * V_j
+ * where K_j = k_cache[block_table[s, j/P], g, j%P, :] and V_j likewise.
+ * The chunk's own K/V must already be in the cache (cpa_kv_write).
+ *   q: device [T, Hq, d] bf16.   k_cache, v_cache: device [NB, Hkv, P, d].
+ *   block_table: device [num_seqs, max_blocks_per_seq] int32.
+ *   out: device [T, Hq, d], bf16 or fp32 per desc->out_dtype.
+ *   workspace: the buffer passed to cpa_plan_upload for this plan.
+ * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax.
+ */
+cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Host-side bounds check of metadata before it is trusted on the device:
+ * every slot_mapping entry is < 0 or < NB*P and no slot repeats; every
+ * block_table entry a sequence can reach (j < ceil(seq_len/P)) is in
+ * [0, NB); lengths as in cpa_plan_create. Any pointer may be NULL to skip
+ * that check. Returns CPA_ERR_INVALID_ARG naming the first bad entry.
+ */
+cpa_status cpa_validate_metadata(const cpa_layer_desc* desc,
+                                 const int32_t* slot_mapping, int32_t num_tokens,
+                                 const int32_t* block_table,
+                                 const int32_t* query_lens,
+                                 const int32_t* seq_lens, int32_t num_seqs);
+
+/* ---- Chunk-size predictor ([CPP]; pure host fp64, no GPU needed) ---- */
+
+/*
+ * base_chunk_size: the base chunk (the profile's largest size).
+ * align: alignment quantum ([CPP] "runtime": a page-size multiple).
+ * min_chunk: floor after alignment ([CPP]: at least 64).
+ * max_chunk: cap ([CPP]: max_num_scheduled_tokens).
+ * max_model_len: cap on L + chunk ([CPP]: max_model_len - history_len).
+ * smooth_factor: s in xs = s*x + (1-s)*base ([CPP] "runtime" names the
+ *   blend but prints no formula; this linear blend is the reading taken).
+ */
+typedef struct cpa_predictor_cfg {
+  int64_t base_chunk_size;
+  int64_t align;
+  int64_t min_chunk;
+  int64_t max_chunk;
+  int64_t max_model_len;
+  double smooth_factor;
+} cpa_predictor_cfg;
+
+/*
+ * [CPP] "startup: profiling": n distinct sizes spread evenly from base down
+ * to lo: sizes[i] = round(base - i*(base-lo)/(n-1)). n >= 2, base > lo >= 1.
+ */
+cpa_status cpa_predictor_profile_sizes(int64_t base, int32_t n, int64_t lo,
+                                       int64_t* sizes);
+
+/*
+ * [CPP] "quadratic latency model" + "startup": least-squares fit of
+ * ms ~ a*l^2 + b*l + c over n >= 3 points (fp64, columns scaled by the
+ * largest |l|). CPA_ERR_NUMERIC if the points are non-finite or do not
+ * determine three coefficients.
+ */
+cpa_status cpa_predictor_fit(const double* lens, const double* ms, int32_t n,
+                             double* a, double* b, double* c);
+
+/* [CPP] "runtime": T = f(base) - f(0) = a*base^2 + b*base. */
+cpa_status cpa_predictor_target(const cpa_predictor_cfg* cfg, double a,
+                                double b, double* T);
+
+/*
+ * [CPP] "runtime": chunk size for the next chunk at prefix history_len with
+ * `remaining` prompt tokens left. x is the positive root of
+ * a*x^2 + (2aL+b)*x - T = 0 (quadratic formula); if a <= 0 or a value is
+ * non-finite, x = T/b when b > 0, else base. Then xs = s*x + (1-s)*base,
+ * xi = floor(xs + 1e-6), aligned down to `align`, raised to min_chunk and
+ * capped at max_chunk, max_model_len - history_len and remaining (never
+ * below 0). *raw_x (may be NULL) receives x.
+ */
+cpa_status cpa_predictor_next_chunk(const cpa_predictor_cfg* cfg, double a,
+                                    double b, double T, int64_t history_len,
+                                    int64_t remaining, int64_t* chunk,
+                                    double* raw_x);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPA_H_ */

@@ -1,0 +1,37 @@
+"""GPU-test plumbing: run a seeded batch through libcpa (device.DeviceBatch)
+and compare with the fp64 oracle at the stated tolerance."""
+from __future__ import annotations
+
+import numpy as np
+
+from chunked_prefill_attention_slot_amd.device import (DeviceBatch, from_dev_u16,  # noqa: F401
+                                                       to_dev_i32, to_dev_u16)
+from oracle.attention import paged_attention
+from oracle.kv_cache import kv_write
+
+# Attention parity bar: max |gpu - oracle| and mean |gpu - oracle| over
+# every compared output element (bf16 inputs, fp32 accumulation, bf16 P in
+# the second product, bf16 or fp32 output).
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def oracle_out(b, rows=None):
+    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+    return paged_attention(b.q, kc, vc, b.block_table, b.query_lens, b.seq_lens,
+                           b.num_kv_heads, b.page_size, rows=rows)
+
+
+def compare(got: np.ndarray, ref: np.ndarray, label: str = ""):
+    """Element-wise comparison on the rows the oracle computed."""
+    mask = ~np.isnan(ref)
+    assert mask.any()
+    assert np.isfinite(got[mask]).all(), f"{label}: non-finite output"
+    err = np.abs(got[mask] - ref[mask])
+    mx, mean = float(err.max()), float(err.mean())
+    full = np.where(mask, np.abs(got - np.nan_to_num(ref)), 0)
+    worst = np.unravel_index(int(np.argmax(full)), full.shape)
+    print(f"[parity] {label}: max_abs={mx:.3e} mean_abs={mean:.3e} worst(token,head,d)={worst}",
+          flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (label, mx, mean, worst)
+    return mx, mean

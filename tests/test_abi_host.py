@@ -1,0 +1,199 @@
+"""Host-side tests of libcpa (no GPU): the library loads and exports every
+symbol include/cpa.h declares; the C++ predictor returns the oracle's chunk
+sizes bit for bit; the planner and validator accept and reject what cpa.h
+says they do."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="session")
+def cpa():
+    from chunked_prefill_attention_slot_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from chunked_prefill_attention_slot_amd import binding
+    return binding
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "cpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(cpa):
+    declared = header_functions()
+    assert len(declared) >= 13
+    assert set(declared) == set(cpa.EXPORTS)
+    for name in declared:
+        assert hasattr(cpa._lib, name), name
+    assert "gfx950" in cpa.cpa_version()
+
+
+# ---- predictor: C++ vs oracle ------------------------------------------
+
+def test_profile_sizes_match_oracle(cpa):
+    from oracle.predictor import profile_sizes
+    for base, n, lo in [(2048, 64, 32), (4096, 64, 1), (1000, 7, 3), (513, 64, 17)]:
+        assert cpa.cpa_predictor_profile_sizes(base, n, lo) == profile_sizes(base, n, lo)
+
+
+def test_target_bit_exact(cpa):
+    from oracle.predictor import target
+    cfg = cpa.predictor_cfg()
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        a, b = float(rng.uniform(-1e-6, 1e-5)), float(rng.uniform(-1e-3, 1e-2))
+        assert cpa.cpa_predictor_target(cfg, a, b) == target(a, b, 2048)
+
+
+@pytest.mark.parametrize("align,smooth", [(128, 1.0), (16, 1.0), (128, 0.7), (1, 0.25)])
+def test_next_chunk_bit_exact_over_grid(cpa, align, smooth):
+    from oracle.predictor import PredictorConfig, next_chunk, target
+    ocfg = PredictorConfig(align=align, smooth_factor=smooth)
+    ccfg = cpa.predictor_cfg(align=align, smooth_factor=smooth)
+    rng = np.random.default_rng(align)
+    coefs = [(a, b) for a in (1e-8, 1e-7, 3.3e-7, 1e-6, 1e-5) for b in (0.0, 1e-4, 7.7e-4, 1e-2)]
+    coefs += [(0.0, 1e-3), (-1e-7, 1e-3), (-1e-7, -1.0), (float("nan"), 1e-3),
+              (1e-6, float("inf")), (1.234e-7, 7.77e-4)]
+    for a, b in coefs:
+        T = target(a, b, 2048) if math.isfinite(a) and math.isfinite(b) else 3.0
+        Ls = list(range(0, 32768, 97)) + [int(x) for x in rng.integers(0, 40000, 50)]
+        for L in Ls:
+            rem = int(rng.integers(0, 40000))
+            got = cpa.cpa_predictor_next_chunk(ccfg, a, b, T, L, rem)
+            exp = next_chunk(ocfg, a, b, T, L, rem)
+            assert got[0] == exp[0], (a, b, L, rem)
+            assert (got[1] == exp[1]) or (math.isnan(got[1]) and math.isnan(exp[1]))
+
+
+def test_walk_matches_oracle(cpa):
+    from oracle.predictor import PredictorConfig, schedule, target
+    a, b = 1e-6, 1e-3
+    T = target(a, b, 2048)
+    walk = schedule(PredictorConfig(), a, b, T, 32768)
+    cfg = cpa.predictor_cfg()
+    L = 0
+    for (Lo, co, xo) in walk:
+        assert L == Lo
+        c, x = cpa.cpa_predictor_next_chunk(cfg, a, b, T, L, 32768 - L)
+        assert c == co and x == xo
+        L += c
+    assert L == 32768
+
+
+def test_fit_matches_oracle(cpa):
+    from oracle.predictor import fit_quadratic, profile_sizes
+    l = np.array(profile_sizes(2048), dtype=float)
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        a, b, c = 10 ** rng.uniform(-8, -5), 10 ** rng.uniform(-4, -2), rng.uniform(0.01, 1)
+        t = a * l * l + b * l + c
+        if trial % 2:
+            t = t + rng.normal(0, 0.01 * c, l.size)
+        got = cpa.cpa_predictor_fit(l, t)
+        exp = fit_quadratic(l, t)
+        for g, e in zip(got, exp):
+            assert abs(g - e) <= 1e-9 * max(abs(e), 1e-300) + 1e-12 * float(np.abs(t).max())
+
+
+def test_fit_rejects_degenerate(cpa):
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_predictor_fit([1.0, 2.0], [1.0, 2.0])
+    assert e.value.status == cpa.CPA_ERR_INVALID_ARG
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_predictor_fit([5.0, 5.0, 5.0, 5.0], [1.0, 2.0, 3.0, 4.0])
+    assert e.value.status == cpa.CPA_ERR_NUMERIC
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_predictor_fit([1.0, 2.0, float("nan")], [1.0, 2.0, 3.0])
+    assert e.value.status == cpa.CPA_ERR_NUMERIC
+
+
+# ---- planner and validator -------------------------------------------------
+
+def desc(cpa, **kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+                num_blocks=200, max_blocks_per_seq=128)
+    base.update(kw)
+    return cpa.layer_desc(**base)
+
+
+def test_plan_rejects_bad_shapes(cpa):
+    cases = [
+        (dict(head_dim=96), cpa.CPA_ERR_UNSUPPORTED),
+        (dict(num_q_heads=30, num_kv_heads=8), cpa.CPA_ERR_INVALID_ARG),
+        (dict(page_size=100), cpa.CPA_ERR_UNSUPPORTED),
+        (dict(page_size=8), cpa.CPA_ERR_UNSUPPORTED),
+        (dict(scale=float("nan")), cpa.CPA_ERR_NUMERIC),
+        (dict(out_dtype=7), cpa.CPA_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(cpa.CpaError) as e:
+            cpa.cpa_plan_create(desc(cpa, **kw), [4], [10])
+        assert e.value.status == status, kw
+        assert cpa.cpa_last_error()
+
+
+def test_plan_rejects_bad_lengths(cpa):
+    d = desc(cpa)
+    for ql, sl in [([5], [4]), ([-1], [4]), ([1], [128 * 128 + 1])]:
+        with pytest.raises(cpa.CpaError) as e:
+            cpa.cpa_plan_create(d, ql, sl)
+        assert e.value.status == cpa.CPA_ERR_INVALID_ARG
+
+
+def test_plan_counts_and_pairs(cpa):
+    d = desc(cpa)
+    for H in (0, 4096, 12288):
+        p = cpa.cpa_plan_create(d, [512], [H + 512])
+        info = p.info()
+        assert info["num_tokens"] == 512
+        assert info["visible_pairs"] == 32 * (512 * H + 512 * 513 // 2)
+        # GQA 4 packs 4 heads x 32 queries per tile: 8 kv heads x 16 tiles
+        tiles = 8 * 16
+        assert info["num_prefill_items"] >= tiles
+        assert info["num_decode_items"] == 0
+        if info["num_combine_items"]:
+            assert info["num_partial_rows"] > 0
+    p = cpa.cpa_plan_create(d, [512], [12800], {"prefill_split": 1})
+    assert p.info()["num_combine_items"] == 0
+    assert p.info()["num_prefill_items"] == 128
+
+
+def test_plan_mixed_batch(cpa):
+    d = desc(cpa, num_q_heads=40, num_kv_heads=40, num_blocks=1200, max_blocks_per_seq=64)
+    ql = [1] * 3 + [512, 0]
+    sl = [1024, 5000, 8192, 2560, 77]
+    p = cpa.cpa_plan_create(d, ql, sl, {"decode_split_keys": 512})
+    info = p.info()
+    assert info["num_tokens"] == 515
+    exp_dec = 40 * sum((n + 511) // 512 for n in sl[:3])
+    assert info["num_decode_items"] == exp_dec
+    assert info["num_prefill_items"] >= 40 * 4
+    pairs = sum(40 * (q * (n - q) + q * (q + 1) // 2) for q, n in zip(ql, sl))
+    assert info["visible_pairs"] == pairs
+
+
+def test_validate_metadata(cpa):
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    b = make_batch(3, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                   query_lens=[5, 1], seq_lens=[40, 17], extra_pages=2)
+    d = cpa.layer_desc(4, 2, 64, 16, b.num_blocks, b.max_blocks_per_seq)
+    cpa.cpa_validate_metadata(d, b.slot_mapping, b.block_table, b.query_lens, b.seq_lens)
+    sm = b.slot_mapping.copy()
+    sm[1] = sm[0]
+    with pytest.raises(cpa.CpaError, match="repeats"):
+        cpa.cpa_validate_metadata(d, sm)
+    sm[1] = b.num_blocks * 16
+    with pytest.raises(cpa.CpaError, match="outside"):
+        cpa.cpa_validate_metadata(d, sm)
+    bt = b.block_table.copy()
+    bt[0, 1] = b.num_blocks
+    with pytest.raises(cpa.CpaError, match="block_table"):
+        cpa.cpa_validate_metadata(d, None, bt, b.query_lens, b.seq_lens)

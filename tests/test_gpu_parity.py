@@ -1,0 +1,184 @@
+"""GPU parity: libcpa's HIP path against the fp64 oracle, element by element,
+through the C ABI. Every test prints its case before touching the GPU."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def H():
+    from tests import gpu_helpers
+    return gpu_helpers
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def make(**kw):
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    return make_batch(**kw)
+
+
+# ---- KV write ------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [
+    dict(seed=1, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+         query_lens=[64], seq_lens=[256]),
+    dict(seed=2, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+         query_lens=[512], seq_lens=[4608], extra_pages=8),
+    dict(seed=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+         query_lens=[1, 7, 0, 33], seq_lens=[50, 7, 3, 100], extra_pages=3),
+])
+def test_kv_write_bit_exact(H, case):
+    from oracle.kv_cache import kv_write
+    b = make(**case)
+    sm = b.slot_mapping.copy()
+    if b.num_tokens > 3:
+        sm[2] = -1                       # a padding token: skipped
+        b.slot_mapping = sm
+    banner(f"kv_write {case}")
+    db = H.DeviceBatch(b)
+    db.kv_write()
+    torch.cuda.synchronize()
+    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+    np.testing.assert_array_equal(H.from_dev_u16(db.k_cache), kc)
+    np.testing.assert_array_equal(H.from_dev_u16(db.v_cache), vc)
+
+
+# ---- attention, full comparison at sizes the oracle finishes quickly ------
+
+def run_and_compare(H, b, label, out_dtype=0, options=None, rows=None):
+    banner(label)
+    db = H.DeviceBatch(b, out_dtype=out_dtype, options=options)
+    db.run()
+    ref = H.oracle_out(b, rows=rows)
+    H.compare(db.out_f64(), ref, label)
+    return db
+
+
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_small_single_sequence(H, out_dtype):
+    """4/4 heads, d=64, H=192 cached in 16-token pages (permuted), C=64."""
+    from chunked_prefill_attention_slot_amd.inputs import small_parity
+    run_and_compare(H, small_parity(), f"small d64 H192 C64 out={out_dtype}", out_dtype)
+
+
+SHAPES = [
+    # hq, hkv, d, P, query_lens, seq_lens
+    (8, 8, 128, 16, [200], [200]),                    # H=0, two row tiles, ragged
+    (32, 8, 128, 128, [300], [1300]),                 # GQA 4, page 128
+    (64, 8, 128, 128, [130], [2178]),                 # GQA 8
+    (16, 1, 64, 32, [45], [333]),                     # MQA 16, d=64
+    (4, 2, 64, 16, [1, 1, 77, 1, 5], [90, 1, 200, 513, 5]),   # decode + prefill mix
+    (40, 40, 128, 128, [1] * 4 + [129], [700, 129, 2000, 4100, 1000]),
+    (12, 4, 128, 64, [3, 0, 2], [3, 9, 300]),         # tiny chunks, empty row
+    (32, 2, 128, 16, [1, 1], [100, 1000]),            # decode GQA 16 -> MFMA kernel
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_random_shapes(H, shape):
+    hq, hkv, d, P, ql, sl = shape
+    b = make(seed=sum(sl) % 1000, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+             page_size=P, query_lens=ql, seq_lens=sl, extra_pages=2)
+    run_and_compare(H, b, f"shape {shape}")
+
+
+def test_forced_splits_agree(H):
+    b = make(seed=7, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+             query_lens=[256], seq_lens=[3000], extra_pages=1)
+    outs = []
+    for split in (1, 3, 7):
+        db = run_and_compare(H, b, f"split {split}", options={"prefill_split": split})
+        outs.append(db.out_f64())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-2
+
+
+def test_decode_split_sizes_agree(H):
+    b = make(seed=8, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
+             query_lens=[1, 1, 1], seq_lens=[5000, 129, 2048])
+    for dsk in (128, 512, 8192):
+        run_and_compare(H, b, f"decode split {dsk}", options={"decode_split_keys": dsk})
+
+
+def test_page_permutation_is_bitwise(H):
+    b = make(seed=9, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+             query_lens=[70, 1], seq_lens=[300, 90], extra_pages=5)
+    banner("page permutation")
+    db = H.DeviceBatch(b)
+    db.run()
+    first = db.out.clone()
+    perm = np.random.default_rng(0).permutation(b.num_blocks)
+    b.k_cache = np.empty_like(b.k_cache); b.k_cache[perm] = H.from_dev_u16(db.k_cache)
+    b.v_cache = np.empty_like(b.v_cache); b.v_cache[perm] = H.from_dev_u16(db.v_cache)
+    b.block_table = np.where(b.block_table >= 0, perm[np.maximum(b.block_table, 0)], -1)
+    b.slot_mapping[:] = -1          # caches already hold every token
+    db2 = H.DeviceBatch(b)
+    db2.run()
+    assert torch.equal(first, db2.out)
+
+
+def test_constant_v_returns_v(H):
+    b = make(seed=10, num_q_heads=8, num_kv_heads=4, head_dim=64, page_size=16,
+             query_lens=[100, 1], seq_lens=[150, 300], extra_pages=1)
+    one = np.uint16(0x3F80)
+    b.v_cache[...] = one
+    b.v_new[...] = one
+    banner("constant V")
+    db = H.DeviceBatch(b, out_dtype=1)
+    db.run()
+    assert np.abs(db.out_f64() - 1.0).max() <= 1e-5
+
+
+def test_attention_requires_upload(H):
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    b = make(seed=11, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+             query_lens=[8], seq_lens=[8])
+    banner("attention without upload")
+    db = H.DeviceBatch(b)
+    other = cpa.cpa_plan_create(db.desc, [4], [8])
+    cpa.cpa_plan_upload(other, db.workspace)      # replaces db.plan in the workspace
+    with pytest.raises(cpa.CpaError) as e:
+        db.attention()
+    assert e.value.status == cpa.CPA_ERR_WORKSPACE
+
+
+# ---- full-size workloads, checked on sampled rows ---------------------------
+
+def sample_rows(ql, k, seed):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, ql - 1, ql // 2, min(ql - 1, 31), min(ql - 1, 32)}
+    return sorted(fixed | set(int(x) for x in rng.integers(0, ql, k)))
+
+
+@pytest.mark.parametrize("hist", [0, 4096, 8192, 12288])
+def test_llama3_8b_chunk512(H, hist):
+    """32 q / 8 kv heads, d=128, page 128, C=512 at prefix H (launch
+    configuration of the bench)."""
+    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
+    b = llama3_8b_chunk(hist)
+    run_and_compare(H, b, f"llama3-8b C512 H{hist}", rows={0: sample_rows(512, 24, hist)})
+
+
+def test_llama13b_mixed_batch(H):
+    """16 decode rows (seq_len U[1024, 8192]) + 2 prefill chunks of 512 at
+    H=2048 and 6144; 40/40 heads, d=128, page 128."""
+    from chunked_prefill_attention_slot_amd.inputs import mixed_llama13b
+    b = mixed_llama13b()
+    rows = {s: [0] for s in range(16)}
+    rows[16] = sample_rows(512, 12, 1)
+    rows[17] = sample_rows(512, 12, 2)
+    run_and_compare(H, b, "llama13b mixed", rows=rows)
+
+
+@pytest.mark.parametrize("hist", [0, 30720])
+def test_long_context_chunk2048(H, hist):
+    """64 q / 8 kv heads, d=128, C=2048 at prefix H (max_model_len 32768)."""
+    from chunked_prefill_attention_slot_amd.inputs import long_context_chunk
+    b = long_context_chunk(hist)
+    run_and_compare(H, b, f"70b-like C2048 H{hist}", rows={0: sample_rows(2048, 12, hist)})
