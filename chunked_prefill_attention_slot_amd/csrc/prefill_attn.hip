@@ -219,20 +219,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m_run * sl2e - msc);
     m_run = m_new;
 
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2e, -msc));
-        sacc[kb][i] = p;
-        lsum += p;
-      }
-    l_run = fmaf(l_run, alpha, lsum);
+      for (int i = 0; i < 16; ++i)
+        sacc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2e, -msc));
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+    // The row sum adds the same bf16-rounded weights the second product
+    // multiplies, so every output row is an exact convex combination of V.
+    float lsum = 0.f;
 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -240,8 +239,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       for (int h2 = 0; h2 < 2; ++h2) {
         u32x4 pw;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
           pw[j] = pack_bf16x2(sacc[kb][8 * h2 + 2 * j], sacc[kb][8 * h2 + 2 * j + 1]);
+          lsum += __uint_as_float(pw[j] << 16) + __uint_as_float(pw[j] & 0xFFFF0000u);
+        }
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
         const int b0 = 8 * kb + 4 * h2 + hh;
 #pragma unroll
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pb, oacc[db]);
         }
       }
+    l_run = fmaf(l_run, alpha, lsum);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
