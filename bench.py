@@ -75,13 +75,13 @@ def headline(args):
     from chunked_prefill_attention_slot_amd.device import DeviceBatch
 
     dbs = []
-    for h in HIST_SWEEP:
+    for h in args.hist:
         b = llama3_8b_chunk(h)
         db = DeviceBatch(b)
         dbs.append((h, db))
         log(f"[bench] llama3-8b C{CHUNK} H{h}: plan {db.plan.info()}")
     hq, d = 32, 128
-    flops = [flops_chunk(hq, d, CHUNK, h) for h in HIST_SWEEP]
+    flops = [flops_chunk(hq, d, CHUNK, h) for h in args.hist]
 
     def step():
         for _, db in dbs:
@@ -112,7 +112,7 @@ def headline(args):
     wall = time.perf_counter() - t0
     per_h = []
     attn_ms_tot = 0.0
-    for i, h in enumerate(HIST_SWEEP):
+    for i, h in enumerate(args.hist):
         a = sorted(s.elapsed_time(e) for s, e in ev_attn[i])
         kv = sorted(s.elapsed_time(e) for s, e in ev_kv[i])
         am = sum(a) / len(a)
@@ -337,6 +337,8 @@ def main():
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--hist", type=int, nargs="+", default=list(HIST_SWEEP),
+                    help="prefixes of the headline sweep (profiling subsets)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -357,7 +359,7 @@ def main():
         "config": {"workload": "Llama-3-8B attention layer (32 q / 8 kv heads, d=128), "
                                "page 128, one 512-token chunk at each H in 0/4096/8192/12288; "
                                "KV write + attention per chunk",
-                   "chunk": CHUNK, "hist": list(HIST_SWEEP), "page_size": 128},
+                   "chunk": CHUNK, "hist": list(args.hist), "page_size": 128},
         "roofline": head["roofline"], "per_H": head["per_H"],
     }
     if not args.no_decode or args.extras:

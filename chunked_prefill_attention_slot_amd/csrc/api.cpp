@@ -38,6 +38,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultCus = 256;
+constexpr int kNumXcds = 8;
 constexpr int kMinSplitKeys = 1024;
 constexpr int kDefaultDecodeSplit = 512;
 
@@ -150,10 +151,57 @@ void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, in
   }
 }
 
-void order_longest_first(std::vector<cpa::WorkItem>& v) {
-  std::stable_sort(v.begin(), v.end(), [](const cpa::WorkItem& x, const cpa::WorkItem& y) {
-    return (x.kv1 - x.kv0) > (y.kv1 - y.kv0);
-  });
+int64_t item_cost(const cpa::WorkItem& w) {
+  return (int64_t)(w.kv1 - w.kv0) * std::max(1, w.nq * w.nheads);
+}
+
+// Order work items for the hardware dispatcher, which hands workgroup i to
+// XCD i % 8: items that read the same KV head of the same sequence are kept
+// on one XCD (one L2), affinity groups are spread over the XCDs longest
+// first, and inside an XCD the costliest items go first.
+void order_for_xcds(std::vector<cpa::WorkItem>& v, int nxcd) {
+  if (v.size() <= 1) return;
+  std::vector<std::pair<int64_t, std::vector<cpa::WorkItem>>> groups;
+  std::unordered_map<int64_t, size_t> index;
+  for (const cpa::WorkItem& w : v) {
+    const int64_t key = ((int64_t)w.seq << 32) | (uint32_t)w.kvh;
+    auto it = index.find(key);
+    if (it == index.end()) {
+      it = index.emplace(key, groups.size()).first;
+      groups.push_back({0, {}});
+    }
+    groups[it->second].first += item_cost(w);
+    groups[it->second].second.push_back(w);
+  }
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const auto& x, const auto& y) { return x.first > y.first; });
+  std::vector<std::vector<cpa::WorkItem>> bins(nxcd);
+  std::vector<int64_t> load(nxcd, 0);
+  for (auto& g : groups) {
+    const int b = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[b] += g.first;
+    bins[b].insert(bins[b].end(), g.second.begin(), g.second.end());
+  }
+  for (auto& b : bins) {
+    std::stable_sort(b.begin(), b.end(), [](const cpa::WorkItem& x, const cpa::WorkItem& y) {
+      return item_cost(x) > item_cost(y);
+    });
+    std::reverse(b.begin(), b.end());  // pop from the back = costliest first
+  }
+  std::vector<cpa::WorkItem> out;
+  out.reserve(v.size());
+  while (out.size() < v.size()) {
+    const int x = (int)(out.size() % nxcd);
+    int b = x;
+    if (bins[b].empty()) {
+      b = 0;
+      for (int k = 1; k < nxcd; ++k)
+        if (bins[k].size() > bins[b].size()) b = k;
+    }
+    out.push_back(bins[b].back());
+    bins[b].pop_back();
+  }
+  v.swap(out);
 }
 
 }  // namespace
@@ -235,23 +283,32 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
     tok += ql;
   }
 
-  // Split long prefill key ranges when the tiles alone cannot fill the GPU.
+  // Split long prefill key ranges when the tiles alone cannot give every
+  // compute unit one work item (one 8-wave item fills a CU); the piece size
+  // is the smallest that keeps all items in a single round. Items are also
+  // split so none touches more than kPrefillPageCap block-table entries.
   const int cus = opt.num_cus > 0 ? opt.num_cus : cpa::kDefaultCus;
-  const int target = opt.target_items > 0 ? opt.target_items : 2 * cus;
-  int64_t total_keys = 0;
-  for (const Tile& t : tiles) total_keys += t.kv_len;
-  int64_t chunk_keys = INT64_MAX;
+  const int target = opt.target_items > 0 ? opt.target_items : cus;
+  const int64_t page_cap_keys =
+      ((int64_t)(cpa::kPrefillPageCap - 1) * desc->page_size) / cpa::kSplitAlign * cpa::kSplitAlign;
+  int64_t chunk_keys = page_cap_keys;
   if (opt.prefill_split == 0 && (int64_t)tiles.size() < target && !tiles.empty()) {
-    chunk_keys = (int64_t)cpa::round_up((size_t)((total_keys + target - 1) / target),
-                                        cpa::kSplitAlign);
-    chunk_keys = std::max<int64_t>(chunk_keys, cpa::kMinSplitKeys);
+    int64_t total_keys = 0;
+    for (const Tile& t : tiles) total_keys += t.kv_len;
+    int64_t c = (int64_t)cpa::round_up((size_t)((total_keys + target - 1) / target),
+                                       cpa::kSplitAlign);
+    c = std::max<int64_t>(c, cpa::kMinSplitKeys);
+    auto count = [&](int64_t ck) {
+      int64_t items = 0;
+      for (const Tile& t : tiles) items += (t.kv_len + ck - 1) / ck;
+      return items;
+    };
+    while (count(c) > target) c += cpa::kSplitAlign;
+    chunk_keys = std::min(chunk_keys, c);
   }
   for (const Tile& t : tiles) {
-    int nsplit = 1;
-    if (opt.prefill_split > 0)
-      nsplit = opt.prefill_split;
-    else if (chunk_keys != INT64_MAX)
-      nsplit = (int)((t.kv_len + chunk_keys - 1) / chunk_keys);
+    int nsplit = (int)((t.kv_len + chunk_keys - 1) / chunk_keys);
+    if (opt.prefill_split > 0) nsplit = std::max(nsplit, opt.prefill_split);
     add_split(p, p->prefill, t, nsplit, cpa::kSplitAlign);
   }
 
@@ -266,11 +323,11 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
       add_split(p, p->decode, t, (n + dsk - 1) / dsk, 1);
     }
   }
-  order_longest_first(p->prefill);
-  order_longest_first(p->decode);
+  order_for_xcds(p->prefill, cpa::kNumXcds);
+  order_for_xcds(p->decode, cpa::kNumXcds);
 
-  // Workspace: [prefill items][decode items][combine items][partial O][partial m,l]
-  size_t off = 0;
+  // Workspace: [zeros][prefill items][decode items][combine items][partial O][partial m,l]
+  size_t off = cpa::kZeroBytes;
   p->off_prefill = off;
   off = cpa::round_up(off + p->prefill.size() * sizeof(cpa::WorkItem), cpa::kAlign);
   p->off_decode = off;
@@ -383,6 +440,7 @@ cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache, cons
   a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
   a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
+  a.zeros = reinterpret_cast<const uint16_t*>(ws);
 
   hipError_t e = cpa::launch_prefill(
       reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_prefill), (int)plan->prefill.size(), a,

@@ -46,12 +46,18 @@ struct AttnArgs {
   int32_t out_f32;
   float* part_o;            // [rows, d] fp32
   float* part_ml;           // [rows, 2] fp32: max (log2 units), sum
+  const uint16_t* zeros;    // >= 16 zero bytes: source for keys past a range
 };
 
-// Prefill tiles hold 128 packed rows (query x head) per work item.
-constexpr int kPrefillRows = 128;
+// Prefill work items: 8 waves of 32 packed rows (query x head) each.
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillRows = 32 * kPrefillWaves;
+// Block-table entries one prefill item may touch (staged in LDS).
+constexpr int kPrefillPageCap = 2048;
 // Key ranges of split items start on multiples of this.
 constexpr int kSplitAlign = 128;
+// Bytes of zeros at the start of the workspace.
+constexpr int kZeroBytes = 256;
 
 hipError_t launch_prefill(const WorkItem* items, int num_items,
                           const AttnArgs& a, int head_dim, hipStream_t stream);

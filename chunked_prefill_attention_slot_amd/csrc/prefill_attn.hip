@@ -8,25 +8,34 @@
 // H+i and sees keys 0..H+i), and the paged-cache metadata of the Ascend
 // dual-stream article, section 3.1 (block_table, seq_lens, query_lens).
 //
-// Work item = 128 packed rows (queries x heads of one GQA group that share
-// a KV head) over one key range. Four waves; wave w owns packed rows
-// 32w..32w+31. Per 64-key tile (128 keys when d = 64):
-//   * K rows are staged in LDS as [key][d] (16-byte chunks XOR-swizzled),
-//     V as [d][key] (8-byte quads XOR-swizzled), both gathered through
-//     block_table by all 256 threads with 16-byte loads, prefetched into
-//     registers one tile ahead;
+// Work item = 256 packed rows (queries x heads of one GQA group that share
+// a KV head) over one key range; eight waves, two per SIMD, so one wave's
+// softmax runs on the vector ALU while the other's products run on the
+// matrix core. Wave w owns packed rows 32w..32w+31. Per 64-key tile:
+//   * K and V rows ([key][d], as in the cache pages) are copied straight
+//     from HBM into LDS with global_load_lds_dwordx4 (no register staging),
+//     gathered through the block-table entries the item touches (staged in
+//     LDS once), double-buffered: tile t+1 is in flight while t is used;
+//     16-byte chunks are XOR-swizzled per row to keep the reads below free
+//     of bank conflicts;
 //   * S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS,
-//     the wave's Q fragment the B operand kept in registers), so that each
-//     lane ends up holding scores of ONE query for 16 keys per 32-key
-//     block: the row max needs one cross-lane swap, and the bf16 P values
-//     already sit in the B-operand layout of the next product;
+//     the wave's Q fragment the B operand kept in registers): each lane then
+//     holds the scores of ONE query for 16 keys of every 32-key block, so
+//     the row max needs one permlane32 swap, and the bf16 weights already
+//     sit in the B-operand layout of the second product;
 //   * the causal mask is applied only on tiles that cross the diagonal or
 //     the end of the key range (select -inf);
 //   * online softmax in fp32 with exp2 (scale*log2(e) folded into one FMA);
-//   * O^T += V^T.P^T on the same MFMA (V^T from LDS, P^T from registers).
-// The order of keys inside a tile is permuted consistently between the K
-// rows fed to the first product and the V slots read for the second one;
-// a contraction does not depend on the order of its terms.
+//     the running max is only raised when a tile exceeds it by more than
+//     2^8, so the rescale of O is rare (weights stay below 256, exact in
+//     the final normalisation);
+//   * O^T += V^T.P^T on the same MFMA; the V^T operand comes from the [key][d]
+//     tile with ds_read_b64_tr_b16, which hands each lane four consecutive
+//     keys of one d column.
+// The rows of K fed to the first product are the tile's keys with bits 2
+// and 3 of the index swapped; that makes each lane's eight accumulators of
+// one 16-key half-block eight consecutive keys, the order the transposed V
+// reads deliver. A contraction does not depend on the order of its terms.
 #include <math.h>
 
 #include "cpa_internal.h"
@@ -36,22 +45,27 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define CPA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 template <int D>
-struct Tile {
-  static constexpr int CH = D / 8;        // 16-byte chunks per key row
-  static constexpr int RPP = 256 / CH;    // key rows per load pass
-  static constexpr int BN = 4 * RPP;      // keys per tile (each thread: 4)
-  static constexpr int NKB = BN / 32;     // 32-key MFMA blocks per tile
-  static constexpr int NKS = D / 16;      // 16-wide d steps of K.Q^T
-  static constexpr int NDB = D / 32;      // 32-row d blocks of V^T.P^T
-  static constexpr int K_BYTES = BN * D * 2;
-  static constexpr int V_BYTES = D * BN * 2;
-  static constexpr int RPP_LOG2 = (RPP == 16) ? 4 : 5;
+struct Cfg {
+  static constexpr int NW = kPrefillWaves;
+  static constexpr int BN = 64;                // keys per tile
+  static constexpr int ROWB = D * 2;           // bytes per key row
+  static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
+  static constexpr int RPI = 1024 / ROWB;      // rows per wave DMA instruction
+  static constexpr int IPW = TILE / 1024 / NW; // DMA instructions per wave per matrix
+  static constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
+  static constexpr int NKS = D / 16;           // 16-wide d steps of K.Q^T
+  static constexpr int NDB = D / 32;           // 32-row d blocks of V^T.P^T
+  static_assert(IPW >= 1, "tile too small for the wave count");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -63,28 +77,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Swizzle of the 16-byte chunk index of K row r: spreads the 8 rows one
-// ds_read_b128 phase touches over distinct bank groups.
-template <int RPP_LOG2>
+// 16-byte chunk swizzle of K row r. The eight lanes of one ds_read_b128
+// phase read rows {0,1,2,3,8,9,10,11} (+4, +16, +32k) at the same logical
+// chunk; these land on distinct bank groups.
+template <int CPR>
 __device__ __forceinline__ int k_swz(int r) {
-  return ((r >> RPP_LOG2) & 3) | ((r & 1) << 2);
+  if constexpr (CPR == 16) return (r & 3) | ((r >> 1) & 4) | ((r & 4) << 1);
+  return (r & 3) | ((r >> 1) & 4);
 }
-// Swizzle of the 8-byte key-quad index of V^T row d.
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 15; }
+// 16-byte chunk swizzle of V row r: a transposed read touches four
+// consecutive rows at two neighbouring chunks; XOR with 0,2,4,6 spreads
+// them over eight distinct chunks.
+__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     const WorkItem* __restrict__ items, AttnArgs a) {
-  using TL = Tile<D>;
-  constexpr int CH = TL::CH, RPP = TL::RPP, BN = TL::BN, NKB = TL::NKB,
-                NKS = TL::NKS, NDB = TL::NDB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TL::K_BYTES + TL::V_BYTES];
-  uint8_t* const Ks = smem;
-  uint8_t* const Vt = smem + TL::K_BYTES;
+  using C = Cfg<D>;
+  constexpr int NW = C::NW, BN = C::BN, ROWB = C::ROWB, CPR = C::CPR, TILE = C::TILE,
+                RPI = C::RPI, IPW = C::IPW, NKB = C::NKB, NKS = C::NKS, NDB = C::NDB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];  // [buffer][K | V]
+  __shared__ int32_t s_pages[kPrefillPageCap];
 
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const float sl2e = a.scale_log2e;
 
@@ -108,102 +126,98 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
   }
 
-  // Loader: thread owns 16-byte chunk lc of key rows lr0 + RPP*p, p < 4.
-  const int lc = tid % CH, lr0 = tid / CH;
-  const int32_t* bt = a.block_table + (size_t)it.seq * a.bt_stride;
-  const int plog = a.page_log2;
-  const int pmask = (1 << plog) - 1;
+  // Stage the block-table entries of this item's key range.
   const int j_end = min(it.kv1, it.hist + it.q0 + it.nq);
-  u32x4 kr[4], vr[4];
+  const int plog = a.page_log2, pmask = (1 << plog) - 1;
+  const int page0 = it.kv0 >> plog;
+  if (it.kv0 < j_end) {
+    const int npages = ((j_end - 1) >> plog) - page0 + 1;
+    const int32_t* bt = a.block_table + (size_t)it.seq * a.bt_stride + page0;
+    for (int i = tid; i < npages; i += 64 * NW) {
+      const int32_t pg = bt[i];
+      s_pages[i] = ((unsigned)pg < (unsigned)a.num_blocks) ? pg : -1;
+    }
+  }
+  __syncthreads();
 
-  auto load_tile = [&](int j0) {
+  // DMA of one tile: wave w issues instructions w*IPW + u of each matrix;
+  // lane -> (row, physical chunk); keys past j_end read a zero block.
+  const int lrow = lane / CPR, lpc = lane % CPR;
+  auto issue = [&](int j0, int buf) {
+    uint8_t* kbuf = smem + buf * 2 * TILE;
+    uint8_t* vbuf = kbuf + TILE;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = j0 + lr0 + RPP * p;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    for (int u = 0; u < IPW; ++u) {
+      const int i = w * IPW + u;
+      const int row = i * RPI + lrow;
+      const int key = j0 + row;
+      const uint16_t* ks = a.zeros;
+      const uint16_t* vs = a.zeros;
       if (key < j_end) {
-        const int page = bt[key >> plog];
-        if ((unsigned)page < (unsigned)a.num_blocks) {
-          const size_t off =
-              ((((size_t)page * a.num_kv_heads + it.kvh) << plog) + (key & pmask)) * D +
-              (size_t)lc * 8;
-          kv = *reinterpret_cast<const u32x4*>(a.k_cache + off);
-          vv = *reinterpret_cast<const u32x4*>(a.v_cache + off);
+        const int pg = s_pages[(key >> plog) - page0];
+        if (pg >= 0) {
+          const size_t base =
+              ((((size_t)pg * a.num_kv_heads + it.kvh) << plog) + (key & pmask)) * D;
+          ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
+          vs = a.v_cache + base + (lpc ^ v_swz(row)) * 8;
         }
       }
-      kr[p] = kv;
-      vr[p] = vv;
+      __builtin_amdgcn_global_load_lds(ks, CPA_LDS(kbuf + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, CPA_LDS(vbuf + i * 1024), 16, 0, 0);
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = lr0 + RPP * p;
-      *reinterpret_cast<u32x4*>(Ks + row * (D * 2) +
-                                ((lc ^ k_swz<TL::RPP_LOG2>(row)) * 16)) = kr[p];
-    }
-    // V^T: key lr0 + RPP*p goes to slot 4*lr0 + p of row d.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * lc + e;
-      const int wd = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (vr[0][wd] >> 16) | (vr[1][wd] & 0xFFFF0000u);
-        hi = (vr[2][wd] >> 16) | (vr[3][wd] & 0xFFFF0000u);
-      } else {
-        lo = (vr[0][wd] & 0xFFFFu) | (vr[1][wd] << 16);
-        hi = (vr[2][wd] & 0xFFFFu) | (vr[3][wd] << 16);
-      }
-      u32x2 q2 = {lo, hi};
-      *reinterpret_cast<u32x2*>(Vt + d * (BN * 2) + ((lr0 ^ v_swz(d)) * 8)) = q2;
-    }
-  };
-
-  float m_run = -INFINITY;  // running max of raw scores of this row
-  float l_run = 0.f;        // this lane's part of the running sum
+  float m_used = -INFINITY;  // reference max of this row (raw score units)
+  float l_run = 0.f;         // this lane's part of the row sum
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  // A-operand row of K.Q^T for MFMA row m = n: key 8kb + 4(m>>4) +
-  // 2((m>>3)&1) + ((m>>2)&1) + RPP*(m&3). Accumulator i of lane half hh then
-  // holds key 8kb + 2(i>>2) + hh + RPP*(i&3).
-  const int krow0 = 4 * (n >> 4) + 2 * ((n >> 3) & 1) + ((n >> 2) & 1) + RPP * (n & 3);
+  // K row fed as A-operand row n of a 32-key block: n with bits 2, 3 swapped.
+  const int krow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
+  // Transposed V reads: 16-lane group g covers d0 = 16(g&1) of each 32-d
+  // block and keys 8(g>>1) + 4u + (s>>2) of each 16-key half block; lane s
+  // of the group supplies the address of d0 + 4(s&3) .. +3 of its key.
+  const int vg = lane >> 4, vs_ = lane & 15;
+  const int vd_off = 16 * (vg & 1) + 4 * (vs_ & 3);
+  const int vkey_off = 8 * (vg >> 1) + (vs_ >> 2);
 
-  if (it.kv0 < j_end) load_tile(it.kv0);
-  for (int j0 = it.kv0; j0 < j_end; j0 += BN) {
+  const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
+  if (ntiles > 0) issue(it.kv0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = it.kv0 + t * BN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j0 + BN < j_end) load_tile(j0 + BN);
+    if (t + 1 < ntiles) issue(j0 + BN, (t + 1) & 1);
+    const uint8_t* Ks = smem + (t & 1) * 2 * TILE;
+    const uint8_t* Vs = Ks + TILE;
 
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int row = krow0 + 8 * kb;
-      const uint8_t* kp = Ks + row * (D * 2);
-      const int sw = k_swz<TL::RPP_LOG2>(row);
+      const int row = 32 * kb + krow;
+      const uint8_t* kp = Ks + row * ROWB;
+      const int sw = k_swz<CPR>(row);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kp + (((2 * ks + hh) ^ sw) * 16));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kp + (((2 * ks + hh) ^ sw) << 4));
         sacc[kb] = mfma32(av, qf[ks], sacc[kb]);
       }
     }
 
-    // Causal mask offset by H, and the end of the key range.
+    // Causal mask offset by H, and the end of the key range. Accumulator i
+    // of lane half hh holds key j0 + 32kb + 16(i>>3) + 8hh + (i&7).
     const bool need_mask = (j0 + BN - 1 > it.hist + it.q0) || (j0 + BN > it.kv1);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = j0 + 8 * kb + 2 * (i >> 2) + hh + RPP * (i & 3);
+          const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
           if (!(key <= qpos && key < it.kv1)) sacc[kb][i] = -INFINITY;
         }
     }
@@ -213,53 +227,77 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float msc = (m_new == -INFINITY) ? 0.f : m_new * sl2e;
-    const float alpha = __builtin_amdgcn_exp2f(m_run * sl2e - msc);
-    m_run = m_new;
-
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    }
+    // Raise the reference max only when a score would exceed it by 2^8.
+    const bool grow = mx * sl2e > m_used * sl2e + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = fmaxf(m_used, mx);
+      const float alpha =
+          (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2e);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_used = m_new;
+    }
+    const float msc = (m_used == -INFINITY) ? 0.f : m_used * sl2e;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         sacc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2e, -msc));
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
-    // The row sum adds the same bf16-rounded weights the second product
-    // multiplies, so every output row is an exact convex combination of V.
-    float lsum = 0.f;
-
+    // O^T += V^T.P^T. The row sum adds the same bf16-rounded weights the
+    // product multiplies, so each output row is a convex combination of V.
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4 pw;
+        // Pairs are built as bf16x2 values and fed to fdot2 directly: passing
+        // an element bit-cast out of a u32x4 made the compiler read the first
+        // element for all four dot products.
+        bf16x2 pp[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pw[j] = pack_bf16x2(sacc[kb][8 * h2 + 2 * j], sacc[kb][8 * h2 + 2 * j + 1]);
-          lsum += __uint_as_float(pw[j] << 16) + __uint_as_float(pw[j] & 0xFFFF0000u);
+          pp[j] = bf16x2{(__bf16)sacc[kb][8 * h2 + 2 * j], (__bf16)sacc[kb][8 * h2 + 2 * j + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
         }
+        const u32x4 pw = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+                          __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const int b0 = 8 * kb + 4 * h2 + hh;
+        const int key0 = 32 * kb + 16 * h2 + vkey_off;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + n;
-          const uint8_t* vp = Vt + d * (BN * 2);
-          const int sw = v_swz(d);
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp + ((b0 ^ sw) * 8));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + (((b0 + 2) ^ sw) * 8));
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          const int d = 32 * db + vd_off;
+          i16x4 part[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int row = key0 + 4 * u;
+            const uint8_t* p = Vs + row * ROWB + (((d >> 3) ^ v_swz(row)) << 4) + ((d & 7) << 1);
+            part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(p));
+          }
+          const u32x4 av = {__builtin_bit_cast(u32x2, part[0])[0],
+                            __builtin_bit_cast(u32x2, part[0])[1],
+                            __builtin_bit_cast(u32x2, part[1])[0],
+                            __builtin_bit_cast(u32x2, part[1])[1]};
           oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pb, oacc[db]);
         }
       }
-    l_run = fmaf(l_run, alpha, lsum);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_tot;
+  {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                     __float_as_uint(l_run), false, false);
+    l_tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
   if (!row_ok) return;
   if (it.part < 0) {
     const float inv = 1.f / l_tot;
@@ -291,7 +329,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         *reinterpret_cast<f32x4*>(a.part_o + prow * D + d) = o4;
       }
     if (hh == 0) {
-      a.part_ml[prow * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * sl2e;
+      a.part_ml[prow * 2 + 0] = (m_used == -INFINITY) ? -INFINITY : m_used * sl2e;
       a.part_ml[prow * 2 + 1] = l_tot;
     }
   }
@@ -302,10 +340,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 hipError_t launch_prefill(const WorkItem* items, int num_items, const AttnArgs& a,
                           int head_dim, hipStream_t stream) {
   if (num_items == 0) return hipSuccess;
+  const dim3 block(64 * kPrefillWaves);
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(num_items), dim3(256), 0, stream, items, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3(num_items), block, 0, stream, items, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(num_items), dim3(256), 0, stream, items, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3(num_items), block, 0, stream, items, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
