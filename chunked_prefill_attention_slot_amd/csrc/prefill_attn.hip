@@ -51,8 +51,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-#define CPA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
 template <int D>
 struct Cfg {
   static constexpr int NW = kPrefillWaves;
@@ -75,6 +73,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// One 16-byte global -> LDS copy per lane: lane i's bytes land at LDS
+// address lds + 16*i. Issued through inline assembly so that the compiler
+// does not order every later LDS read behind it (it cannot tell the two
+// tile buffers apart); completion is awaited explicitly with vmcnt before
+// the barrier that publishes a tile.
+// m0 (which holds the LDS address) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 // 16-byte chunk swizzle of K row r. The eight lanes of one ds_read_b128
@@ -124,6 +141,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       if (row_ok) v = qrow[2 * ks + hh];
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
+    // Wait for Q here (vmcnt 0): a wait the compiler would otherwise place
+    // at the first product inside the tile loop would also stall on the
+    // next tile's DMA.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // Stage the block-table entries of this item's key range.
@@ -143,9 +164,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   // DMA of one tile: wave w issues instructions w*IPW + u of each matrix;
   // lane -> (row, physical chunk); keys past j_end read a zero block.
   const int lrow = lane / CPR, lpc = lane % CPR;
+  const uint32_t smem_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto issue = [&](int j0, int buf) {
-    uint8_t* kbuf = smem + buf * 2 * TILE;
-    uint8_t* vbuf = kbuf + TILE;
+    const uint32_t kbuf = smem_lds + buf * 2 * TILE;
+    const uint32_t vbuf = kbuf + TILE;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
       const int i = w * IPW + u;
@@ -162,8 +185,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           vs = a.v_cache + base + (lpc ^ v_swz(row)) * 8;
         }
       }
-      __builtin_amdgcn_global_load_lds(ks, CPA_LDS(kbuf + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, CPA_LDS(vbuf + i * 1024), 16, 0, 0);
+      lds_dma16(ks, __builtin_amdgcn_readfirstlane(kbuf + i * 1024));
+      lds_dma16(vs, __builtin_amdgcn_readfirstlane(vbuf + i * 1024));
     }
   };
 
