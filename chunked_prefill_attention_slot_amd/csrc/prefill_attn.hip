@@ -38,6 +38,8 @@
 // reads deliver. A contraction does not depend on the order of its terms.
 #include <math.h>
 
+#include <type_traits>
+
 #include "cpa_internal.h"
 
 namespace cpa {
@@ -63,8 +65,13 @@ struct Cfg {
   static constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
   static constexpr int NKS = D / 16;           // 16-wide d steps of K.Q^T
   static constexpr int NDB = D / 32;           // 32-row d blocks of V^T.P^T
+  static constexpr int NBUF = 3;               // LDS tile buffers
+  static constexpr int V_REGION = NBUF * TILE; // V tiles follow the K tiles
   static_assert(IPW >= 1, "tile too small for the wave count");
 };
+
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -102,18 +109,25 @@ __device__ __forceinline__ int k_swz(int r) {
   if constexpr (CPR == 16) return (r & 3) | ((r >> 1) & 4) | ((r & 4) << 1);
   return (r & 3) | ((r >> 1) & 4);
 }
-// 16-byte chunk swizzle of V row r: a transposed read touches four
-// consecutive rows at two neighbouring chunks; XOR with 0,2,4,6 spreads
-// them over eight distinct chunks.
-__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
+// 16-byte chunk swizzle of V row r. A transposed read by 16 lanes touches
+// four consecutive rows at two neighbouring chunks, 32 lanes the same rows
+// at four chunks; XOR with 0, 6, 10, 12 (d = 128) spreads either set over
+// distinct bank groups (XOR with 0, 2, 4, 6 for the 8-chunk rows of d = 64).
+template <int CPR>
+__device__ __forceinline__ int v_swz(int r) {
+  if constexpr (CPR == 16) return (0xCA60u >> (4 * (r & 3))) & 15;
+  return (r & 3) << 1;
+}
 
 template <int D>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     const WorkItem* __restrict__ items, AttnArgs a) {
   using C = Cfg<D>;
   constexpr int NW = C::NW, BN = C::BN, ROWB = C::ROWB, CPR = C::CPR, TILE = C::TILE,
-                RPI = C::RPI, IPW = C::IPW, NKB = C::NKB, NKS = C::NKS, NDB = C::NDB;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];  // [buffer][K | V]
+                RPI = C::RPI, IPW = C::IPW, NKB = C::NKB, NKS = C::NKS, NDB = C::NDB,
+                V_REGION = C::V_REGION;
+  // [K tile 0..2][V tile 0..2]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::NBUF * TILE];
   __shared__ int32_t s_pages[kPrefillPageCap];
 
   const WorkItem it = items[blockIdx.x];
@@ -166,9 +180,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int lrow = lane / CPR, lpc = lane % CPR;
   const uint32_t smem_lds =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue = [&](int j0, int buf) {
-    const uint32_t kbuf = smem_lds + buf * 2 * TILE;
-    const uint32_t vbuf = kbuf + TILE;
+  auto issue = [&](int j0, int buf) __attribute__((always_inline)) {
+    const uint32_t kbuf = smem_lds + buf * TILE;
+    const uint32_t vbuf = smem_lds + V_REGION + buf * TILE;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
       const int i = w * IPW + u;
@@ -182,13 +196,35 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           const size_t base =
               ((((size_t)pg * a.num_kv_heads + it.kvh) << plog) + (key & pmask)) * D;
           ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
-          vs = a.v_cache + base + (lpc ^ v_swz(row)) * 8;
+          vs = a.v_cache + base + (lpc ^ v_swz<CPR>(row)) * 8;
         }
       }
       lds_dma16(ks, __builtin_amdgcn_readfirstlane(kbuf + i * 1024));
       lds_dma16(vs, __builtin_amdgcn_readfirstlane(vbuf + i * 1024));
     }
   };
+
+  // Per-lane LDS offsets of the operand reads; the tile buffer and the
+  // 32-key block add compile-time constants.
+  // K: A-operand row n of a 32-key block is key n with bits 2, 3 swapped;
+  // accumulator i of lane half hh then holds key 32kb + 16(i>>3) + 8hh + (i&7).
+  const int krow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
+  int kofs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    kofs[ks] = krow * ROWB + (((2 * ks + hh) ^ k_swz<CPR>(krow)) << 4);
+  // V^T by transposed reads: 16-lane group g covers d 16(g&1) .. +15 of each
+  // 32-d block and keys 8(g>>1) + 4u + (s>>2) of each 16-key half block;
+  // lane s of the group supplies the address of d 4(s&3) .. +3 of its key.
+  const int vg = lane >> 4, vl = lane & 15;
+  const int vd_off = 16 * (vg & 1) + 4 * (vl & 3);
+  const int vkey_off = 8 * (vg >> 1) + (vl >> 2);
+  int vofs[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    vofs[db] = V_REGION + vkey_off * ROWB +
+               (((4 * db + (vd_off >> 3)) ^ v_swz<CPR>(vkey_off)) << 4) + ((vd_off & 7) << 1);
+  const auto* smem3 = (const __attribute__((address_space(3))) uint8_t*)smem;
 
   float m_used = -INFINITY;  // reference max of this row (raw score units)
   float l_run = 0.f;         // this lane's part of the row sum
@@ -198,66 +234,52 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  // K row fed as A-operand row n of a 32-key block: n with bits 2, 3 swapped.
-  const int krow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
-  // Transposed V reads: 16-lane group g covers d0 = 16(g&1) of each 32-d
-  // block and keys 8(g>>1) + 4u + (s>>2) of each 16-key half block; lane s
-  // of the group supplies the address of d0 + 4(s&3) .. +3 of its key.
-  const int vg = lane >> 4, vs_ = lane & 15;
-  const int vd_off = 16 * (vg & 1) + 4 * (vs_ & 3);
-  const int vkey_off = 8 * (vg >> 1) + (vs_ >> 2);
-
-  const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
-  if (ntiles > 0) issue(it.kv0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = it.kv0 + t * BN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) issue(j0 + BN, (t + 1) & 1);
-    const uint8_t* Ks = smem + (t & 1) * 2 * TILE;
-    const uint8_t* Vs = Ks + TILE;
-
-    f32x16 sacc[NKB];
+  // S^T = K.Q^T for the tile in buffer B.
+  auto s_tile = [&](auto bc, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int row = 32 * kb + krow;
-      const uint8_t* kp = Ks + row * ROWB;
-      const int sw = k_swz<CPR>(row);
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kp + (((2 * ks + hh) ^ sw) << 4));
-        sacc[kb] = mfma32(av, qf[ks], sacc[kb]);
+        const bf16x8 av =
+            *reinterpret_cast<const bf16x8*>(smem + (B * TILE + 32 * kb * ROWB) + kofs[ks]);
+        acc = mfma32(av, qf[ks], acc);
       }
+      s[kb] = acc;
     }
+  };
 
-    // Causal mask offset by H, and the end of the key range. Accumulator i
-    // of lane half hh holds key j0 + 32kb + 16(i>>3) + 8hh + (i&7).
-    const bool need_mask = (j0 + BN - 1 > it.hist + it.q0) || (j0 + BN > it.kv1);
-    if (need_mask) {
+  // Causal mask offset by H, and the end of the key range. Accumulator i
+  // of lane half hh holds key j0 + 32kb + 16(i>>3) + 8hh + (i&7).
+  auto mask = [&](f32x16 (&s)[NKB], int j0) __attribute__((always_inline)) {
+    if ((j0 + BN - 1 > it.hist + it.q0) || (j0 + BN > it.kv1)) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if (!(key <= qpos && key < it.kv1)) sacc[kb][i] = -INFINITY;
+          if (!(key <= qpos && key < it.kv1)) s[kb][i] = -INFINITY;
         }
     }
-
+  };
+  // Row max over both lane halves (same query).
+  auto row_max = [&](const f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-    }
-    // Raise the reference max only when a score would exceed it by 2^8.
-    const bool grow = mx * sl2e > m_used * sl2e + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+  };
+  // Raise the reference max only when a score would exceed it by 2^8 (rare;
+  // O and l are rescaled then). Returns the exponent offset of the weights.
+  auto raise_max = [&](float mx) __attribute__((always_inline)) -> float {
+    if (__builtin_amdgcn_ballot_w64(mx * sl2e > m_used * sl2e + 8.f)) {
       const float m_new = fmaxf(m_used, mx);
       const float alpha =
           (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2e);
@@ -268,51 +290,120 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_used = m_new;
     }
-    const float msc = (m_used == -INFINITY) ? 0.f : m_used * sl2e;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        sacc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2e, -msc));
+    return (m_used == -INFINITY) ? 0.f : m_used * sl2e;
+  };
 
-    // O^T += V^T.P^T. The row sum adds the same bf16-rounded weights the
-    // product multiplies, so each output row is a convex combination of V.
+  // Weights in bf16, packed in the B-operand layout of V^T.P^T. The row sum
+  // adds the same bf16-rounded weights the product multiplies, so each
+  // output row is a convex combination of V. Pairs go to fdot2 as bf16x2
+  // values (bit-casting elements of a u32x4 into it was miscompiled into
+  // four reads of the first element).
+  auto weights = [&](const f32x16 (&s)[NKB], float msc, u32x4 (&pw)[NKB][2])
+                     __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        // Pairs are built as bf16x2 values and fed to fdot2 directly: passing
-        // an element bit-cast out of a u32x4 made the compiler read the first
-        // element for all four dot products.
-        bf16x2 pp[4];
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pp[j] = bf16x2{(__bf16)sacc[kb][8 * h2 + 2 * j], (__bf16)sacc[kb][8 * h2 + 2 * j + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h2 + 2 * j], sl2e, -msc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h2 + 2 * j + 1], sl2e, -msc));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+          pw[kb][h2][j] = __builtin_bit_cast(uint32_t, pp);
         }
-        const u32x4 pw = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
-                          __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const int key0 = 32 * kb + 16 * h2 + vkey_off;
+  };
+
+  // O^T += V^T.P^T for the tile in buffer B.
+  auto pv_tile = [&](auto bc, const u32x4 (&pw)[NKB][2]) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kb][h2]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + vd_off;
-          i16x4 part[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int row = key0 + 4 * u;
-            const uint8_t* p = Vs + row * ROWB + (((d >> 3) ^ v_swz(row)) << 4) + ((d & 7) << 1);
-            part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(p));
-          }
-          const u32x4 av = {__builtin_bit_cast(u32x2, part[0])[0],
-                            __builtin_bit_cast(u32x2, part[0])[1],
-                            __builtin_bit_cast(u32x2, part[1])[0],
-                            __builtin_bit_cast(u32x2, part[1])[1]};
+          const int base = vofs[db] + B * TILE + (32 * kb + 16 * h2) * ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(smem3 + base));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(smem3 + base + 4 * ROWB));
+          const u32x4 av = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
           oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pb, oacc[db]);
         }
       }
+  };
+
+  // Software pipeline over three LDS buffers (tile t lives in buffer t % 3)
+  // and two score arrays (tile t's scores in sc[t % 2]). Step t waits for
+  // tile t+1 and starts the copy of tile t+2, then runs
+  //   [scores of tile t+1 on the matrix core | weights of tile t on the VALU]
+  //   [V product of tile t on the matrix core | row max of tile t+1 on the VALU]
+  // and finally the (rare) rescale for tile t+1.
+  const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
+  f32x16 sc[2][NKB];
+  float msc = 0.f;
+  if (ntiles > 0) {
+    issue(it.kv0, 0);
+    if (ntiles > 1) {
+      issue(it.kv0 + BN, 1);
+      if constexpr (2 * IPW == 4)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    s_tile(ic<0>{}, sc[0]);
+    mask(sc[0], it.kv0);
+    msc = raise_max(row_max(sc[0]));
+  }
+  auto step = [&](auto bc, auto pc, int t) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int CUR = decltype(pc)::value, NXT = 1 - CUR;
+    const int j0 = it.kv0 + t * BN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < ntiles) issue(j0 + 2 * BN, (B + 2) % 3);
+    s_tile(ic<(B + 1) % 3>{}, sc[NXT]);  // unused past the last tile
+    u32x4 pw[NKB][2];
+    weights(sc[CUR], msc, pw);
+    // Keep the weights in this block, next to the score products: left
+    // alone, the compiler sinks them past the mask branch below.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) asm volatile("" ::"v"(pw[kb][h2]));
+    // Interleave: per score product, one K read, a few weight
+    // instructions, the product.
+#pragma unroll
+    for (int i = 0; i < NKB * NKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x0002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+    }
+    mask(sc[NXT], j0 + BN);
+    pv_tile(ic<B>{}, pw);
+    const float mx = row_max(sc[NXT]);
+    asm volatile("" ::"v"(mx));  // keep the max next to the V products
+    if (t + 1 < ntiles) msc = raise_max(mx);
+  };
+  for (int t = 0; t < ntiles; t += 6) {
+    step(ic<0>{}, ic<0>{}, t);
+    if (t + 1 >= ntiles) break;
+    step(ic<1>{}, ic<1>{}, t + 1);
+    if (t + 2 >= ntiles) break;
+    step(ic<2>{}, ic<0>{}, t + 2);
+    if (t + 3 >= ntiles) break;
+    step(ic<0>{}, ic<1>{}, t + 3);
+    if (t + 4 >= ntiles) break;
+    step(ic<1>{}, ic<0>{}, t + 4);
+    if (t + 5 >= ntiles) break;
+    step(ic<2>{}, ic<1>{}, t + 5);
   }
 
   float l_tot;
