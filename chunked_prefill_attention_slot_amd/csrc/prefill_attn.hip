@@ -378,18 +378,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) asm volatile("" ::"v"(pw[kb][h2]));
-    // Interleave: per score product, one K read, a few weight
-    // instructions, the product.
+    // Interleave: K reads run three products ahead of their use; each
+    // score product is followed by a few weight instructions.
+    __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);  // DS read
 #pragma unroll
     for (int i = 0; i < NKB * NKS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x0002, 5, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0002, 5, 0);  // VALU
+      if (i + 3 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
     }
     mask(sc[NXT], j0 + BN);
     pv_tile(ic<B>{}, pw);
     const float mx = row_max(sc[NXT]);
     asm volatile("" ::"v"(mx));  // keep the max next to the V products
+    // Transposed V reads run three products ahead of their use.
+    __builtin_amdgcn_sched_group_barrier(0x0100, 6, 1);
+#pragma unroll
+    for (int i = 0; i < NKB * 2 * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x0002, 3, 1);
+      if (i + 3 < NKB * 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
+    }
     if (t + 1 < ntiles) msc = raise_max(mx);
   };
   for (int t = 0; t < ntiles; t += 6) {
