@@ -286,9 +286,10 @@ def predictor_run(args, align=128):
     return res
 
 
-def cpu_baseline(budget_s=20.0):
-    """The fp64 oracle on host cores: the H=12288 Llama-3-8B chunk, query
-    heads taken one at a time until about budget_s seconds have passed."""
+def cpu_baseline(budget_s=10.0):
+    """The fp64 oracle on host cores over the headline step: the Llama-3-8B
+    chunk at H = 0, 4096, 8192, 12288, every query head, repeated until
+    budget_s seconds have passed (whole passes only)."""
     from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
     from oracle.attention import causal_chunk_attention, gather_sequence, widen_bf16
     from oracle.kv_cache import kv_write
@@ -299,33 +300,64 @@ def cpu_baseline(budget_s=20.0):
         threads = max([i["threads"] or 1 for i in blas] or [1])
     except Exception:
         blas, threads = [], os.cpu_count()
-    h = 12288
-    b = llama3_8b_chunk(h)
-    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
-    n = h + CHUNK
+    prepared = []
+    for h in HIST_SWEEP:
+        b = llama3_8b_chunk(h)
+        kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+        prepared.append((h, b, kc, vc))
+    passes = 0
     t0 = time.perf_counter()
-    k = widen_bf16(gather_sequence(kc, b.block_table[0], n, b.page_size))
-    v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size))
-    q = widen_bf16(b.q)
-    heads = 0
-    while heads < 32:
-        g = heads // 4
-        causal_chunk_attention(q[:, heads], k[:, g], v[:, g], h, 1.0 / math.sqrt(128))
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
+    while True:
+        for h, b, kc, vc in prepared:
+            n = h + CHUNK
+            k = widen_bf16(gather_sequence(kc, b.block_table[0], n, b.page_size))
+            v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size))
+            q = widen_bf16(b.q)
+            for head in range(32):
+                causal_chunk_attention(q[:, head], k[:, head // 4], v[:, head // 4], h,
+                                       1.0 / math.sqrt(128))
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    f = flops_chunk(heads, 128, CHUNK, h)
+    f = passes * sum(flops_chunk(32, 128, CHUNK, h) for h in HIST_SWEEP)
     try:
         aff = len(os.sched_getaffinity(0))
     except Exception:
         aff = os.cpu_count()
     res = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"Llama-3-8B chunk C=512 at H=12288, {heads} of 32 query heads "
-                     f"(all 512 rows each), fp64 NumPy, gather included; {dt:.1f} s",
+           "sample": f"{passes} pass(es) of the headline step (Llama-3-8B, C=512 at H=0/4096/"
+                     f"8192/12288, all 32 query heads), fp64 NumPy oracle incl. gather; {dt:.1f} s",
            "seconds": dt, "cpu_count": os.cpu_count(), "affinity": aff, "blas": blas}
-    log(f"[bench] cpu oracle: {heads} heads in {dt:.1f} s -> {res['value']*1e3:.2f} GFLOP/s")
+    log(f"[bench] cpu oracle: {passes} passes in {dt:.1f} s -> {res['value']*1e3:.2f} GFLOP/s")
     return res
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling rocprofv3's FETCH_SIZE /
+    WRITE_SIZE counters into bytes: each launch reads and writes nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
+
+
+def load_traffic(kernel_src):
+    """HBM bytes per launch of the prefill kernel from the committed counter
+    summary, or None if it was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_attn_llama3_8b_c512_traffic.txt")
+    try:
+        fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
+    except OSError:
+        return None, "no counter summary"
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16", "").strip() != sha:
+        return None, "kernel changed since the counters were taken"
+    return float(fields["hbm_bytes_per_launch"]), fields.get("note", "").strip()
 
 
 def main():
@@ -339,6 +371,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--hist", type=int, nargs="+", default=list(HIST_SWEEP),
                     help="prefixes of the headline sweep (profiling subsets)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -347,6 +381,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} CUs={props.multi_processor_count}")
 
@@ -362,6 +399,14 @@ def main():
                    "chunk": CHUNK, "hist": list(args.hist), "page_size": 128},
         "roofline": head["roofline"], "per_H": head["per_H"],
     }
+    traffic, note = load_traffic(os.path.join(ROOT, "chunked_prefill_attention_slot_amd", "csrc",
+                                              "prefill_attn.hip"))
+    out["roofline"]["traffic"] = traffic
+    out["roofline"]["traffic_note"] = note
+    # Algorithmic bytes per launch averaged over the sweep: K and V of every
+    # visible key once, Q in, O out (bf16).
+    alg = sum((h + CHUNK) * 8 * 128 * 2 * 2 + CHUNK * 32 * 128 * 2 * 2 for h in args.hist)
+    out["roofline"]["algorithmic_bytes_per_launch"] = alg / len(args.hist)
     if not args.no_decode or args.extras:
         from chunked_prefill_attention_slot_amd.inputs import mixed_llama13b
         from chunked_prefill_attention_slot_amd.device import DeviceBatch
