@@ -5,7 +5,7 @@
 // sequence, tokens concatenated on one axis, seq_len = prefix + current)
 // into lists of work items for the kernels:
 //   * prefill chunks (query_len >= 2): one item per (sequence, KV head,
-//     head sub-group, 128-row query tile), the key range split into pieces
+//     head sub-group, 256-row query tile), the key range split into pieces
 //     when there are too few tiles to fill the GPU; split tiles also get a
 //     combine item;
 //   * decode rows (query_len == 1): one item per (sequence, KV head, key
@@ -257,7 +257,7 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   const int G = Hq / Hkv;
   p->group = G;
   // Heads packed per prefill tile: the largest power of two dividing G (it
-  // divides the 128 rows); the tile then holds 128/GP queries.
+  // divides the kPrefillRows rows); the tile then holds kPrefillRows/GP queries.
   int GP = 1;
   while (GP < cpa::kPrefillRows && G % (GP * 2) == 0) GP *= 2;
   const int QT = cpa::kPrefillRows / GP;

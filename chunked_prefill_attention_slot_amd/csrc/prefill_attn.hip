@@ -15,7 +15,7 @@
 //   * K and V rows ([key][d], as in the cache pages) are copied straight
 //     from HBM into LDS with global_load_lds_dwordx4 (no register staging),
 //     gathered through the block-table entries the item touches (staged in
-//     LDS once), double-buffered: tile t+1 is in flight while t is used;
+//     LDS once), over three buffers: tile t+2 is in flight while t is used;
 //     16-byte chunks are XOR-swizzled per row to keep the reads below free
 //     of bank conflicts;
 //   * S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS,
