@@ -127,12 +127,11 @@ struct Tile {
 void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, int nsplit,
                int align) {
   cpa::WorkItem base{t.seq, t.kvh, t.head0, t.nheads, t.tok0, t.q0, t.nq, t.hist, 0, t.kv_len, -1, 0};
-  if (nsplit <= 1 || t.kv_len <= align) {
-    out.push_back(base);
-    return;
-  }
-  const int per = (int)cpa::round_up((size_t)((t.kv_len + nsplit - 1) / nsplit), (size_t)align);
-  nsplit = (t.kv_len + per - 1) / per;
+  // The key range is cut into `align`-key units dealt out as evenly as
+  // possible (piece sizes differ by at most one unit), so split items of a
+  // tile finish together.
+  const int units = (t.kv_len + align - 1) / align;
+  nsplit = std::min(nsplit, units);
   if (nsplit <= 1) {
     out.push_back(base);
     return;
@@ -142,12 +141,15 @@ void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, in
   p->part_rows += nsplit * rows;
   p->max_combine_rows = std::max(p->max_combine_rows, rows);
   p->combine.push_back(cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, nsplit, part0, rows, 0});
+  int start = 0;
   for (int k = 0; k < nsplit; ++k) {
+    const int n_units = units / nsplit + (k < units % nsplit ? 1 : 0);
     cpa::WorkItem w = base;
-    w.kv0 = k * per;
-    w.kv1 = std::min(t.kv_len, (k + 1) * per);
+    w.kv0 = start * align;
+    w.kv1 = std::min(t.kv_len, (start + n_units) * align);
     w.part = part0 + k * rows;
     out.push_back(w);
+    start += n_units;
   }
 }
 

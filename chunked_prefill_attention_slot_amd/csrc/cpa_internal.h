@@ -55,7 +55,7 @@ constexpr int kPrefillRows = 32 * kPrefillWaves;
 // Block-table entries one prefill item may touch (staged in LDS).
 constexpr int kPrefillPageCap = 2048;
 // Key ranges of split items start on multiples of this.
-constexpr int kSplitAlign = 128;
+constexpr int kSplitAlign = 64;
 // Bytes of zeros at the start of the workspace.
 constexpr int kZeroBytes = 256;
 

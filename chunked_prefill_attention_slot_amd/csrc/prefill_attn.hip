@@ -176,13 +176,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   __syncthreads();
 
   // DMA of one tile: wave w issues instructions w*IPW + u of each matrix;
-  // lane -> (row, physical chunk); keys past j_end read a zero block.
+  // lane -> (row, physical chunk); keys past j_end read a zero block. The
+  // IPW*RPI rows of one wave lie in one page (pages hold >= 16 keys), so the
+  // page number is one uniform value per wave, looked up ahead of the copy.
+  static_assert(IPW * RPI <= 16, "a wave's rows must fit the smallest page");
   const int lrow = lane / CPR, lpc = lane % CPR;
   const uint32_t smem_lds =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue = [&](int j0, int buf) __attribute__((always_inline)) {
+  auto page_of = [&](int j0) __attribute__((always_inline)) -> int {
+    const int key_w = j0 + w * IPW * RPI;
+    return (key_w < j_end) ? s_pages[(key_w >> plog) - page0] : -1;
+  };
+  auto issue = [&](int j0, int pg, int buf) __attribute__((always_inline)) {
     const uint32_t kbuf = smem_lds + buf * TILE;
     const uint32_t vbuf = smem_lds + V_REGION + buf * TILE;
+    const size_t pbase = ((size_t)(pg < 0 ? 0 : pg) * a.num_kv_heads + it.kvh) << plog;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
       const int i = w * IPW + u;
@@ -190,14 +198,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       const int key = j0 + row;
       const uint16_t* ks = a.zeros;
       const uint16_t* vs = a.zeros;
-      if (key < j_end) {
-        const int pg = s_pages[(key >> plog) - page0];
-        if (pg >= 0) {
-          const size_t base =
-              ((((size_t)pg * a.num_kv_heads + it.kvh) << plog) + (key & pmask)) * D;
-          ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
-          vs = a.v_cache + base + (lpc ^ v_swz<CPR>(row)) * 8;
-        }
+      if (key < j_end && pg >= 0) {
+        const size_t base = (pbase + (key & pmask)) * D;
+        ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
+        vs = a.v_cache + base + (lpc ^ v_swz<CPR>(row)) * 8;
       }
       lds_dma16(ks, __builtin_amdgcn_readfirstlane(kbuf + i * 1024));
       lds_dma16(vs, __builtin_amdgcn_readfirstlane(vbuf + i * 1024));
@@ -233,45 +237,57 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  f32x16 sc[NKB];  // scores of the current tile, from the S phase to the P phase
 
-  // S^T = K.Q^T for the tile in buffer B.
-  auto s_tile = [&](auto bc, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+  // S phase: S^T = K.Q^T for the tile in buffer B; the two 32-key blocks
+  // are accumulated alternately (two independent chains), K reads run four
+  // products ahead.
+  auto s_phase = [&](auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
+    f32x16 acc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      f32x16 acc;
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 av =
             *reinterpret_cast<const bf16x8*>(smem + (B * TILE + 32 * kb * ROWB) + kofs[ks]);
-        acc = mfma32(av, qf[ks], acc);
+        acc[kb] = mfma32(av, qf[ks], acc[kb]);
       }
-      s[kb] = acc;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = acc[kb];
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < NKB * NKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+      if (i + 4 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
     }
   };
 
   // Causal mask offset by H, and the end of the key range. Accumulator i
   // of lane half hh holds key j0 + 32kb + 16(i>>3) + 8hh + (i&7).
-  auto mask = [&](f32x16 (&s)[NKB], int j0) __attribute__((always_inline)) {
+  auto mask = [&](int j0) __attribute__((always_inline)) {
     if ((j0 + BN - 1 > it.hist + it.q0) || (j0 + BN > it.kv1)) {
+      // key = j0 + 8hh + c with c a compile-time constant per accumulator;
+      // the key is visible iff c < lim.
+      const int lim = min(qpos + 1, it.kv1) - j0 - 8 * hh;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if (!(key <= qpos && key < it.kv1)) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 16 * (i >> 3) + (i & 7) >= lim) sc[kb][i] = -INFINITY;
     }
   };
   // Row max over both lane halves (same query).
-  auto row_max = [&](const f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
+  auto row_max = [&]() __attribute__((always_inline)) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
@@ -292,127 +308,143 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     }
     return (m_used == -INFINITY) ? 0.f : m_used * sl2e;
   };
+  // V^T operand of the product for keys 32kb + 16h2 .. +15 and d block db:
+  // two transposed reads of four keys each.
+  auto v_read = [&](int base) __attribute__((always_inline)) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(smem3 + base));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(smem3 + base + 4 * ROWB));
+    const u32x4 av = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    return __builtin_bit_cast(bf16x8, av);
+  };
 
-  // Weights in bf16, packed in the B-operand layout of V^T.P^T. The row sum
-  // adds the same bf16-rounded weights the product multiplies, so each
-  // output row is a convex combination of V. Pairs go to fdot2 as bf16x2
-  // values (bit-casting elements of a u32x4 into it was miscompiled into
-  // four reads of the first element).
-  auto weights = [&](const f32x16 (&s)[NKB], float msc, u32x4 (&pw)[NKB][2])
-                     __attribute__((always_inline)) {
+  // P phase for tile t in buffer B: mask, row max, (rare) rescale, then the
+  // bf16 weights of each 16-key half block, each followed by its four
+  // products O^T += V^T.P^T. The row sum adds the same bf16-rounded weights
+  // the product multiplies, so each output row is a convex combination of
+  // V. Pairs go to fdot2 as bf16x2 values (bit-casting elements of a u32x4
+  // into it was miscompiled into four reads of the first element).
+  auto p_phase = [&](auto bc, int t) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    // The first half block's V operands do not wait for the softmax.
+    bf16x8 vpre[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vpre[db] = v_read(vofs[db] + B * TILE);
+    mask(it.kv0 + t * BN);
+    const float msc = raise_max(row_max());
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x2 pp[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h2 + 2 * j], sl2e, -msc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h2 + 2 * j + 1], sl2e, -msc));
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-          pw[kb][h2][j] = __builtin_bit_cast(uint32_t, pp);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h2 + 2 * j], sl2e, -msc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h2 + 2 * j + 1], sl2e, -msc));
+          pp[j] = bf16x2{(__bf16)p0, (__bf16)p1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
         }
-  };
-
-  // O^T += V^T.P^T for the tile in buffer B.
-  auto pv_tile = [&](auto bc, const u32x4 (&pw)[NKB][2]) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kb][h2]);
+        const u32x4 pw = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+                          __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int base = vofs[db] + B * TILE + (32 * kb + 16 * h2) * ROWB;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(smem3 + base));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(smem3 + base + 4 * ROWB));
-          const u32x4 av = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-          oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pb, oacc[db]);
+          const bf16x8 av = (kb == 0 && h2 == 0)
+                                ? vpre[db]
+                                : v_read(vofs[db] + B * TILE + (32 * kb + 16 * h2) * ROWB);
+          oacc[db] = mfma32(av, pb, oacc[db]);
         }
       }
-  };
-
-  // Software pipeline over three LDS buffers (tile t lives in buffer t % 3)
-  // and two score arrays (tile t's scores in sc[t % 2]). Step t waits for
-  // tile t+1 and starts the copy of tile t+2, then runs
-  //   [scores of tile t+1 on the matrix core | weights of tile t on the VALU]
-  //   [V product of tile t on the matrix core | row max of tile t+1 on the VALU]
-  // and finally the (rare) rescale for tile t+1.
-  const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
-  f32x16 sc[2][NKB];
-  float msc = 0.f;
-  if (ntiles > 0) {
-    issue(it.kv0, 0);
-    if (ntiles > 1) {
-      issue(it.kv0 + BN, 1);
-      if constexpr (2 * IPW == 4)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    s_tile(ic<0>{}, sc[0]);
-    mask(sc[0], it.kv0);
-    msc = raise_max(row_max(sc[0]));
-  }
-  auto step = [&](auto bc, auto pc, int t) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
-    constexpr int CUR = decltype(pc)::value, NXT = 1 - CUR;
-    const int j0 = it.kv0 + t * BN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < ntiles) issue(j0 + 2 * BN, (B + 2) % 3);
-    s_tile(ic<(B + 1) % 3>{}, sc[NXT]);  // unused past the last tile
-    u32x4 pw[NKB][2];
-    weights(sc[CUR], msc, pw);
-    // Keep the weights in this block, next to the score products: left
-    // alone, the compiler sinks them past the mask branch below.
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) asm volatile("" ::"v"(pw[kb][h2]));
-    // Interleave: K reads run three products ahead of their use; each
-    // score product is followed by a few weight instructions.
-    __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);  // DS read
-#pragma unroll
-    for (int i = 0; i < NKB * NKS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x0002, 5, 0);  // VALU
-      if (i + 3 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
-    }
-    mask(sc[NXT], j0 + BN);
-    pv_tile(ic<B>{}, pw);
-    const float mx = row_max(sc[NXT]);
-    asm volatile("" ::"v"(mx));  // keep the max next to the V products
-    // Transposed V reads run three products ahead of their use.
-    __builtin_amdgcn_sched_group_barrier(0x0100, 6, 1);
+    // Weights of the first half block, then per product: the next weights
+    // on the VALU and V reads two products ahead.
+    __builtin_amdgcn_sched_group_barrier(0x0002, 24, 1);  // VALU
 #pragma unroll
     for (int i = 0; i < NKB * 2 * NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x0002, 3, 1);
-      if (i + 3 < NKB * 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0002, 6, 1);  // VALU
+      if (i + 2 < NKB * 2 * NDB - NDB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
     }
-    if (t + 1 < ntiles) msc = raise_max(mx);
   };
-  for (int t = 0; t < ntiles; t += 6) {
-    step(ic<0>{}, ic<0>{}, t);
-    if (t + 1 >= ntiles) break;
-    step(ic<1>{}, ic<1>{}, t + 1);
-    if (t + 2 >= ntiles) break;
-    step(ic<2>{}, ic<0>{}, t + 2);
-    if (t + 3 >= ntiles) break;
-    step(ic<0>{}, ic<1>{}, t + 3);
-    if (t + 4 >= ntiles) break;
-    step(ic<1>{}, ic<0>{}, t + 4);
-    if (t + 5 >= ntiles) break;
-    step(ic<2>{}, ic<1>{}, t + 5);
+
+  // Two wave groups in ping-pong. Group 0 (waves 0..NW/2-1) runs the phases
+  // S(0), P(0), S(1), P(1), ... one per half step; group 1 runs the same
+  // sequence one half step later, so on every SIMD one wave's score
+  // products overlap the other wave's softmax and V products. Tile t lives
+  // in LDS buffer t % 3; K(t) is read in half steps 2t, 2t+1 and V(t) in
+  // 2t+1, 2t+2, so the copy of tile t+3 into the same buffer is issued at
+  // the end of half step 2t+3 and awaited before half step 2t+6.
+  const int grp = w / (NW / 2);
+  const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
+  if (ntiles > 0) {
+    issue(it.kv0, page_of(it.kv0), 0);
+    if (ntiles > 1) issue(it.kv0 + BN, page_of(it.kv0 + BN), 1);
+    if (ntiles > 2) issue(it.kv0 + 2 * BN, page_of(it.kv0 + 2 * BN), 2);
+    const int last = 2 * ntiles;  // half steps 0 .. last
+    // Each group runs its own copy of the loop (same barriers, different
+    // phase order), which keeps the register allocation of the two phase
+    // sequences apart.
+    auto run = [&](auto gc) __attribute__((always_inline)) {
+      constexpr int G = decltype(gc)::value;
+      auto half = [&](auto jc, int h) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;  // h % 6
+        if constexpr (J % 2 == 0) {
+          // Tile s = h/2 must have landed; copies of later tiles stay in flight.
+          const int s = h >> 1;
+          const int newest = (s + 1 >= 3) ? min(ntiles - 1, s + 1) : min(ntiles, 3) - 1;
+          const int ahead = newest - s;
+          if (ahead >= 2) {
+            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          } else if (ahead == 1) {
+            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+          } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+        }
+        __syncthreads();
+        const int tn = (h + 3) >> 1;  // tile copied at the end of an odd half step
+        const bool copy = (J % 2 == 1) && h >= 3 && tn < ntiles;
+        int pg = -1;
+        if (copy) pg = page_of(it.kv0 + tn * BN);
+        if constexpr (G == 0) {
+          // phase h: S(h/2) or P((h-1)/2)
+          if constexpr (J % 2 == 0) {
+            if ((h >> 1) < ntiles) s_phase(ic<J / 2>{});
+          } else {
+            p_phase(ic<J / 2>{}, h >> 1);
+          }
+        } else {
+          // phase h-1: P((h-2)/2) or S((h-1)/2)
+          if constexpr (J % 2 == 0) {
+            if (h >= 1) p_phase(ic<(J / 2 + 2) % 3>{}, (h - 1) >> 1);
+          } else {
+            s_phase(ic<J / 2>{});
+          }
+        }
+        if (copy) issue(it.kv0 + tn * BN, pg, ((J + 3) / 2) % 3);
+      };
+      for (int h0 = 0; h0 <= last; h0 += 6) {
+        half(ic<0>{}, h0);
+        if (h0 + 1 > last) break;
+        half(ic<1>{}, h0 + 1);
+        if (h0 + 2 > last) break;
+        half(ic<2>{}, h0 + 2);
+        if (h0 + 3 > last) break;
+        half(ic<3>{}, h0 + 3);
+        if (h0 + 4 > last) break;
+        half(ic<4>{}, h0 + 4);
+        if (h0 + 5 > last) break;
+        half(ic<5>{}, h0 + 5);
+      }
+    };
+    if (grp == 0)
+      run(ic<0>{});
+    else
+      run(ic<1>{});
   }
 
   float l_tot;
