@@ -63,6 +63,7 @@ struct Cfg {
   static constexpr int RPI = 1024 / ROWB;      // rows per wave DMA instruction
   static constexpr int IPW = TILE / 1024 / NW; // DMA instructions per wave per matrix
   static constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
+  static_assert(NKB == 2, "the row max tree assumes two 32-key blocks");
   static constexpr int NKS = D / 16;           // 16-wide d steps of K.Q^T
   static constexpr int NDB = D / 32;           // 32-row d blocks of V^T.P^T
   static constexpr int NBUF = 3;               // LDS tile buffers
@@ -99,6 +100,28 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
       : "=&s"(saved)
       : "v"(src), "s"(lds)
       : "memory");
+}
+
+// The same copy with a uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (no per-lane address arithmetic).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// Smallest bf16 value >= x (x finite).
+__device__ __forceinline__ float bf16_ceil(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = (x > 0.f) ? ((u + 0xFFFFu) & 0xFFFF0000u) : (u & 0xFFFF0000u);
+  return __uint_as_float(u);
 }
 
 // 16-byte chunk swizzle of K row r. The eight lanes of one ds_read_b128
@@ -144,15 +167,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const bool row_ok = qi < it.nq;
   const int qpos = it.hist + it.q0 + qi;
 
-  // Q fragment: B operand of K.Q^T, lane holds d = 16ks + 8hh .. +7.
+  // Q fragment: B operand of K.Q^T, lane holds d = 16ks + 8hh .. +7,
+  // multiplied by scale*log2(e) and rounded to bf16, so the products are
+  // scores in log2 units (the rounding perturbs a score by far less than
+  // the bf16 rounding of the weights that follows).
   bf16x8 qf[NKS];
   {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(
         a.q + ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D);
+    u32x4 qv[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = qrow[2 * ks + hh];
+      qv[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) qv[ks] = qrow[2 * ks + hh];
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = pack_bf16x2(__uint_as_float(qv[ks][j] << 16) * sl2e,
+                           __uint_as_float(qv[ks][j] & 0xFFFF0000u) * sl2e);
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
     // Wait for Q here (vmcnt 0): a wait the compiler would otherwise place
@@ -185,11 +220,35 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto page_of = [&](int j0) __attribute__((always_inline)) -> int {
     const int key_w = j0 + w * IPW * RPI;
-    return (key_w < j_end) ? s_pages[(key_w >> plog) - page0] : -1;
+    return __builtin_amdgcn_readfirstlane((key_w < j_end) ? s_pages[(key_w >> plog) - page0]
+                                                          : -1);
   };
+  // Byte offsets of this lane's 16 bytes from the wave's first row (row
+  // u*RPI + lrow of the wave's IPW*RPI, chunk swizzled to where it lands).
+  uint32_t koff[IPW], voff[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int row = (w * IPW + u) * RPI + lrow;  // tile row (same low bits)
+    koff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ k_swz<CPR>(row)) * 8) * 2);
+    voff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ v_swz<CPR>(row)) * 8) * 2);
+  }
   auto issue = [&](int j0, int pg, int buf) __attribute__((always_inline)) {
     const uint32_t kbuf = smem_lds + buf * TILE;
     const uint32_t vbuf = smem_lds + V_REGION + buf * TILE;
+    const int key_w = j0 + w * IPW * RPI;
+    if (pg >= 0 && key_w + IPW * RPI <= j_end) {
+      // All rows of this wave are in range: uniform page base in SGPRs.
+      const size_t e0 = ((((size_t)pg * a.num_kv_heads + it.kvh) << plog) + (key_w & pmask)) * D;
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int i = w * IPW + u;
+        lds_dma16_s(a.k_cache + e0, koff[u], kbuf + i * 1024);
+        lds_dma16_s(a.v_cache + e0, voff[u], vbuf + i * 1024);
+      }
+      return;
+    }
+    // Last tile of the range (or an invalid block-table entry): rows past
+    // j_end read a zero block, so masked keys meet finite values.
     const size_t pbase = ((size_t)(pg < 0 ? 0 : pg) * a.num_kv_heads + it.kvh) << plog;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
@@ -230,14 +289,24 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
                (((4 * db + (vd_off >> 3)) ^ v_swz<CPR>(vkey_off)) << 4) + ((vd_off & 7) << 1);
   const auto* smem3 = (const __attribute__((address_space(3))) uint8_t*)smem;
 
-  float m_used = -INFINITY;  // reference max of this row (raw score units)
+  // Reference offset of this row in log2 units: a bf16 value that no score
+  // seen so far exceeds by more than 8 (scores are taken relative to it
+  // inside the score product); unset before the row's first visible key.
+  float m_ref = 0.f;
+  bool unset = true;
   float l_run = 0.f;         // this lane's part of the row sum
+  // Offset product ONES x QOFF adds -m_ref to every score of the column:
+  // the B operand holds -m_ref at k = 0 (lanes of half 0), zeros elsewhere.
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  bf16x8 qoff = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f,
+                 (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  f32x16 sc[NKB];  // scores of the current tile, from the S phase to the P phase
+  f32x16 sc[NKB];  // scores - m_ref (log2 units) of the current tile, S -> P phase
 
   // S phase: S^T = K.Q^T for the tile in buffer B; the two 32-key blocks
   // are accumulated alternately (two independent chains), K reads run four
@@ -245,10 +314,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   auto s_phase = [&](auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
     f32x16 acc[NKB];
+    const f32x16 zero = {};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
+    for (int kb = 0; kb < NKB; ++kb) acc[kb] = mfma32(ones, qoff, zero);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -259,7 +327,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sc[kb] = acc[kb];
-    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);    // DS read
+    __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);  // offset products
 #pragma unroll
     for (int i = 0; i < NKB * NKS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
@@ -283,30 +352,44 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   };
   // Row max over both lane halves (same query).
   auto row_max = [&]() __attribute__((always_inline)) -> float {
-    float mx = -INFINITY;
+    // Balanced tree: a written chain of maxima stays serial.
+    float m8[8];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int j = 0; j < 8; ++j)
+      m8[j] = fmaxf(fmaxf(sc[0][2 * j], sc[0][2 * j + 1]), fmaxf(sc[1][2 * j], sc[1][2 * j + 1]));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+    for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
+    const float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
   };
-  // Raise the reference max only when a score would exceed it by 2^8 (rare;
-  // O and l are rescaled then). Returns the exponent offset of the weights.
-  auto raise_max = [&](float mx) __attribute__((always_inline)) -> float {
-    if (__builtin_amdgcn_ballot_w64(mx * sl2e > m_used * sl2e + 8.f)) {
-      const float m_new = fmaxf(m_used, mx);
-      const float alpha =
-          (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2e);
+  // Move the reference only when a score would exceed it by more than 8
+  // (weights above 2^8; rare: O and l are rescaled and this tile's scores
+  // shifted), or to the first visible score of the row. The new reference is
+  // rounded up to bf16 so that the offset product represents it exactly.
+  auto raise_ref = [&](float mx) __attribute__((always_inline)) {
+    const bool need = unset ? (mx > -INFINITY) : (mx > 8.f);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float alpha = 1.f, delta = 0.f;
+      if (need) {
+        const float m_new = bf16_ceil(m_ref + mx);
+        alpha = unset ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        delta = m_ref - m_new;
+        m_ref = m_new;
+        unset = false;
+        if (hh == 0) qoff[0] = (__bf16)(-m_ref);
+      }
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_used = m_new;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] += delta;
     }
-    return (m_used == -INFINITY) ? 0.f : m_used * sl2e;
   };
   // V^T operand of the product for keys 32kb + 16h2 .. +15 and d block db:
   // two transposed reads of four keys each.
@@ -320,8 +403,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     return __builtin_bit_cast(bf16x8, av);
   };
 
-  // P phase for tile t in buffer B: mask, row max, (rare) rescale, then the
-  // bf16 weights of each 16-key half block, each followed by its four
+  // P phase for tile t in buffer B: mask, row max, (rare) reference move,
+  // then the bf16 weights 2^(score - m_ref) of each 16-key half block, each followed by its four
   // products O^T += V^T.P^T. The row sum adds the same bf16-rounded weights
   // the product multiplies, so each output row is a convex combination of
   // V. Pairs go to fdot2 as bf16x2 values (bit-casting elements of a u32x4
@@ -333,8 +416,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vpre[db] = v_read(vofs[db] + B * TILE);
     mask(it.kv0 + t * BN);
-    const float msc = raise_max(row_max());
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    raise_ref(row_max());
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -342,10 +425,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         bf16x2 pp[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h2 + 2 * j], sl2e, -msc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h2 + 2 * j + 1], sl2e, -msc));
+          const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j]);
+          const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j + 1]);
           pp[j] = bf16x2{(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, l_run, false);
         }
         const u32x4 pw = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                           __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
@@ -484,7 +567,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         *reinterpret_cast<f32x4*>(a.part_o + prow * D + d) = o4;
       }
     if (hh == 0) {
-      a.part_ml[prow * 2 + 0] = (m_used == -INFINITY) ? -INFINITY : m_used * sl2e;
+      a.part_ml[prow * 2 + 0] = unset ? -INFINITY : m_ref;
       a.part_ml[prow * 2 + 1] = l_tot;
     }
   }
