@@ -32,6 +32,8 @@ EXPORTS = (
     "cpa_plan_destroy", "cpa_plan_get_info", "cpa_plan_upload",
     "cpa_attention", "cpa_validate_metadata", "cpa_predictor_profile_sizes",
     "cpa_predictor_fit", "cpa_predictor_target", "cpa_predictor_next_chunk",
+    "cpa_calib_features", "cpa_calib_fit", "cpa_calib_target", "cpa_calib_next_chunk",
+    "cpa_calib_create", "cpa_calib_destroy", "cpa_calib_record", "cpa_calib_model",
 )
 
 
@@ -109,6 +111,17 @@ _sig("cpa_predictor_target", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
 _sig("cpa_predictor_next_chunk", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
      ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64, ctypes.c_int64,
      _I64P, _F64P)
+_sig("cpa_calib_features", ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _F64P)
+_sig("cpa_calib_fit", ctypes.c_int32, _F64P, _F64P, ctypes.c_int32, _F64P, _F64P, _F64P)
+_sig("cpa_calib_target", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg), ctypes.c_double,
+     ctypes.c_double, ctypes.c_double, _F64P)
+_sig("cpa_calib_next_chunk", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
+     ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+     ctypes.c_int64, _I64P, _F64P)
+_sig("cpa_calib_create", ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P))
+_sig("cpa_calib_destroy", ctypes.c_int32, _P)
+_sig("cpa_calib_record", ctypes.c_int32, _P, _F64P, ctypes.c_double, _I32P)
+_sig("cpa_calib_model", ctypes.c_int32, _P, _F64P, _F64P, _F64P, _I32P)
 
 
 def _check(status: int):
@@ -283,3 +296,65 @@ def cpa_predictor_next_chunk(cfg, a: float, b: float, T: float, history_len: int
     _check(_lib.cpa_predictor_next_chunk(ctypes.byref(cfg), a, b, T, int(history_len),
                                          int(remaining), ctypes.byref(chunk), ctypes.byref(x)))
     return chunk.value, x.value
+
+
+# ---- online calibration ----
+
+def cpa_calib_features(chunk_lens, hist_lens):
+    c = np.ascontiguousarray(chunk_lens, dtype=np.int32)
+    h = np.ascontiguousarray(hist_lens, dtype=np.int32)
+    out = (ctypes.c_double * 3)()
+    _check(_lib.cpa_calib_features(c.ctypes.data_as(_I32P), h.ctypes.data_as(_I32P),
+                                   int(c.shape[0]), out))
+    return tuple(out)
+
+
+def cpa_calib_fit(feats, ms):
+    f = np.ascontiguousarray(feats, dtype=np.float64).reshape(-1, 3)
+    t = np.ascontiguousarray(ms, dtype=np.float64)
+    a, b, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(_lib.cpa_calib_fit(f.ctypes.data_as(_F64P), t.ctypes.data_as(_F64P), int(t.shape[0]),
+                              ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def cpa_calib_target(cfg, a: float, b: float, c: float) -> float:
+    T = ctypes.c_double()
+    _check(_lib.cpa_calib_target(ctypes.byref(cfg), a, b, c, ctypes.byref(T)))
+    return T.value
+
+
+def cpa_calib_next_chunk(cfg, a: float, b: float, c: float, T: float, history_len: int,
+                         remaining: int):
+    chunk = ctypes.c_int64()
+    x = ctypes.c_double()
+    _check(_lib.cpa_calib_next_chunk(ctypes.byref(cfg), a, b, c, T, int(history_len),
+                                     int(remaining), ctypes.byref(chunk), ctypes.byref(x)))
+    return chunk.value, x.value
+
+
+class Calib:
+    """Owns a cpa_calib record window (cpa_calib_create / _destroy)."""
+
+    def __init__(self, min_points: int = 5, window: int = 30):
+        h = _P()
+        _check(_lib.cpa_calib_create(int(min_points), int(window), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib.cpa_calib_destroy(self._h)
+            self._h = None
+
+    def record(self, feat, ms: float) -> bool:
+        f = (ctypes.c_double * 3)(*[float(v) for v in feat])
+        ready = ctypes.c_int32()
+        _check(_lib.cpa_calib_record(self._h, f, float(ms), ctypes.byref(ready)))
+        return bool(ready.value)
+
+    def model(self):
+        a, b, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        n = ctypes.c_int32()
+        _check(_lib.cpa_calib_model(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                    ctypes.byref(n)))
+        return a.value, b.value, c.value

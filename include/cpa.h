@@ -254,6 +254,78 @@ cpa_status cpa_predictor_next_chunk(const cpa_predictor_cfg* cfg, double a,
                                     int64_t remaining, int64_t* chunk,
                                     double* raw_x);
 
+/* ---- Online calibration ([CPP] "online calibration"; host fp64) ---- */
+
+/*
+ * Two-variable latency model f(C, H) = a*C*(C+H) + b*(C+H) + c of a chunk of
+ * C tokens after H tokens of history. An executed batch is recorded by its
+ * feature vector feat = [sum C*(C+H), sum (C+H), N] over its N sequences
+ * with C > 0 ([CPP] prints this vector), so batch time ~ a*feat[0] +
+ * b*feat[1] + c*feat[2]. chunk_lens/hist_lens: host arrays of n entries
+ * (read during the call); hist_lens >= 0. feat: 3 doubles written.
+ */
+cpa_status cpa_calib_features(const int32_t* chunk_lens, const int32_t* hist_lens,
+                              int32_t n, double* feat);
+
+/*
+ * Least squares (a, b, c) over n >= 3 records: feats is row-major [n][3],
+ * ms the measured times (any unit; the coefficients take it). Columns are
+ * scaled by their largest magnitude before the solve. CPA_ERR_NUMERIC for
+ * non-finite input, an all-zero column, or records that do not determine
+ * three coefficients.
+ */
+cpa_status cpa_calib_fit(const double* feats, const double* ms, int32_t n,
+                         double* a, double* b, double* c);
+
+/*
+ * Per-chunk target of the two-variable model: T' = f(base, 0) =
+ * a*base^2 + b*base + c (the latency of a base-size chunk without history;
+ * [CPP] leaves the target of the calibrated model unstated, this is the
+ * reading taken).
+ */
+cpa_status cpa_calib_target(const cpa_predictor_cfg* cfg, double a, double b,
+                            double c, double* T);
+
+/*
+ * Next chunk at prefix history_len under the two-variable model: x is the
+ * positive root of a*x^2 + (a*H + b)*x + (b*H + c - T) = 0 (f(x, H) = T,
+ * quadratic formula); if a <= 0 (all values finite) x = (T - b*H - c) /
+ * (a*H + b) when a*H + b > 0, else base; a negative discriminant or a
+ * non-finite value gives base. Then the post-processing of
+ * cpa_predictor_next_chunk (smoothing, floor(xs + 1e-6), alignment,
+ * min_chunk, caps). *raw_x (may be NULL) receives x.
+ */
+cpa_status cpa_calib_next_chunk(const cpa_predictor_cfg* cfg, double a,
+                                double b, double c, double T,
+                                int64_t history_len, int64_t remaining,
+                                int64_t* chunk, double* raw_x);
+
+/*
+ * Record window of the online calibration ([CPP]: refit by least squares
+ * once enough points, 5 to 30, are held): the `window` most recent records
+ * are kept, and the model is refitted after every record once at least
+ * min_points are held (3 <= min_points <= window). Host object owned by the
+ * caller; not thread-safe.
+ */
+typedef struct cpa_calib_s* cpa_calib;
+cpa_status cpa_calib_create(int32_t min_points, int32_t window, cpa_calib* out);
+cpa_status cpa_calib_destroy(cpa_calib calib);
+
+/*
+ * Adds one record (feat: 3 doubles as from cpa_calib_features; ms its
+ * time). *ready (may be NULL) is set to 1 once a model is available. A
+ * failed refit (CPA_ERR_NUMERIC) keeps the previous model.
+ */
+cpa_status cpa_calib_record(cpa_calib calib, const double* feat, double ms,
+                            int32_t* ready);
+
+/*
+ * Current model. *points (may be NULL) receives the records held.
+ * CPA_ERR_NUMERIC while fewer than min_points records have been fitted.
+ */
+cpa_status cpa_calib_model(cpa_calib calib, double* a, double* b, double* c,
+                           int32_t* points);
+
 #ifdef __cplusplus
 }
 #endif

@@ -197,3 +197,87 @@ def test_validate_metadata(cpa):
     bt[0, 1] = b.num_blocks
     with pytest.raises(cpa.CpaError, match="block_table"):
         cpa.cpa_validate_metadata(d, None, bt, b.query_lens, b.seq_lens)
+
+
+# ---- online calibration: C++ vs oracle ----------------------------------------
+
+def test_calib_features_match_oracle(cpa):
+    from oracle.calibration import features
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        n = int(rng.integers(0, 20))
+        C = rng.integers(-3, 4096, n)
+        H = rng.integers(0, 1 << 20, n)
+        assert cpa.cpa_calib_features(C, H) == features(C, H)
+
+
+def test_calib_fit_matches_oracle(cpa):
+    from oracle.calibration import features, fit
+    rng = np.random.default_rng(8)
+    for trial in range(10):
+        feats, ms = [], []
+        for _ in range(int(rng.integers(5, 31))):
+            N = int(rng.integers(1, 6))
+            C = rng.integers(16, 2048, N)
+            H = rng.integers(0, 30000, N)
+            f = features(C, H)
+            feats.append(f)
+            ms.append(3e-8 * f[0] + 2e-4 * f[1] + 0.03 * f[2] + rng.normal(0, 1e-3))
+        got = cpa.cpa_calib_fit(feats, ms)
+        exp = fit(feats, ms)
+        for g, e in zip(got, exp):
+            assert abs(g - e) <= 1e-9 * max(abs(e), 1e-300) + 1e-12 * max(abs(v) for v in ms)
+
+
+@pytest.mark.parametrize("align,smooth", [(128, 1.0), (16, 1.0), (128, 0.6)])
+def test_calib_next_chunk_bit_exact(cpa, align, smooth):
+    from oracle.calibration import next_chunk, target
+    from oracle.predictor import PredictorConfig
+    ocfg = PredictorConfig(align=align, smooth_factor=smooth)
+    ccfg = cpa.predictor_cfg(align=align, smooth_factor=smooth)
+    rng = np.random.default_rng(align + int(smooth * 10))
+    models = [(a, b, c) for a in (1e-9, 1e-8, 1.3e-7, 1e-6) for b in (0.0, 1e-4, 7.7e-4)
+              for c in (0.0, 0.05, 1.0)]
+    models += [(0.0, 1e-3, 0.1), (-1e-8, 1e-3, 0.1), (-1e-8, -1e-3, 0.1), (float("nan"), 1e-3, 0.1),
+               (1e-7, float("inf"), 0.1)]
+    for a, b, c in models:
+        finite = all(map(np.isfinite, (a, b, c)))
+        T = target(a, b, c, 2048) if finite else 2.0
+        if finite:
+            assert cpa.cpa_calib_target(ccfg, a, b, c) == T
+        for H in list(range(0, 32768, 331)) + [int(v) for v in rng.integers(0, 40000, 40)]:
+            rem = int(rng.integers(0, 40000))
+            got = cpa.cpa_calib_next_chunk(ccfg, a, b, c, T, H, rem)
+            exp = next_chunk(ocfg, a, b, c, T, H, rem)
+            assert got[0] == exp[0], (a, b, c, H, rem)
+            assert got[1] == exp[1] or (np.isnan(got[1]) and np.isnan(exp[1]))
+
+
+def test_calib_window_matches_oracle(cpa):
+    from oracle.calibration import Calibrator, features
+    rng = np.random.default_rng(13)
+    ref = Calibrator(min_points=5, window=12)
+    h = cpa.Calib(min_points=5, window=12)
+    with pytest.raises(cpa.CpaError):
+        h.model()
+    for i in range(40):
+        C = rng.integers(16, 2048, 2)
+        H = rng.integers(0, 20000, 2)
+        f = features(C, H)
+        ms = (1e-8 if i < 20 else 4e-8) * f[0] + 1e-4 * f[1] + 0.02 * f[2] + rng.normal(0, 1e-4)
+        assert h.record(f, ms) == ref.record(f, ms)
+        if ref.coef is not None:
+            for g, e in zip(h.model(), ref.coef):
+                assert abs(g - e) <= 1e-9 * abs(e) + 1e-15
+
+
+def test_calib_rejects_bad_arguments(cpa):
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.Calib(min_points=2, window=30)
+    assert e.value.status == cpa.CPA_ERR_INVALID_ARG
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_calib_fit([[1.0, 2.0, 1.0]] * 4, [1.0, 2.0, 3.0, 4.0])
+    assert e.value.status == cpa.CPA_ERR_NUMERIC
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_calib_features([5], [-1])
+    assert e.value.status == cpa.CPA_ERR_INVALID_ARG
