@@ -226,17 +226,26 @@ def long_context(args):
     return res
 
 
-def predictor_run(args, align=128):
+PREDICTOR_SHAPES = {
+    # the profiling shape of the predictor workload: 4/4 heads, d=64, page 16
+    "tiny": dict(num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16),
+    # a Llama-3-8B attention layer, where the chunk cost grows with history
+    "llama3_8b": dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128),
+}
+
+
+def predictor_run(args, align=128, shape="tiny", prompt=32768):
     """Startup profiling at 64 sizes (2048 down to 32, H=0) of KV write +
-    attention at the 4/4-head d=64 page-16 shape, least-squares fit, target
-    T = f(2048) - f(0), then a 32768-token prompt prefilled with predicted
-    chunks; reports measured/T per chunk."""
+    attention, least-squares fit, target T = f(2048) - f(0), then a prompt
+    prefilled with predicted chunks (one-variable model); then the same
+    prompt again with online calibration of the two-variable model f(C,H)
+    (refitted from each chunk's measured time once 5 are held; before that
+    the one-variable model sizes the chunks). Reports measured/T per chunk."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     from chunked_prefill_attention_slot_amd.inputs import make_batch
     from chunked_prefill_attention_slot_amd.device import DeviceBatch
-    b = make_batch(3, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
-                   query_lens=[32768], seq_lens=[32768])
+    b = make_batch(3, query_lens=[prompt], seq_lens=[prompt], **PREDICTOR_SHAPES[shape])
     db = DeviceBatch(b)
 
     def runner(L, c):
@@ -256,33 +265,78 @@ def predictor_run(args, align=128):
     a, bb, c = cpa.cpa_predictor_fit(sizes, ms)
     cfg = cpa.predictor_cfg(align=align)
     T = cpa.cpa_predictor_target(cfg, a, bb)
+    f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c   # modelled latency of a base chunk at H=0
 
     def f_model(x):
         return a * x * x + bb * x + c
+
+    def summary(chunks, key):
+        r = np.array([cch[key] for cch in chunks])
+        return {"min": float(r.min()), "max": float(r.max()), "mean": float(r.mean()),
+                "cv": float(r.std() / r.mean()),
+                "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1))}
+
     chunks = []
     L = 0
-    while L < 32768:
-        ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, 32768 - L)
+    while L < prompt:
+        ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
         if ch <= 0:
             break
         m = median_ms(runner(L, ch), 11, 2)["median_ms"]
         model_ratio = (f_model(L + ch) - f_model(L)) / T
         chunks.append({"L": L, "chunk": ch, "raw_x": x, "ms": m, "meas_over_T": m / T,
-                       "model_over_T": model_ratio, "meas_over_f_base": m / f_model(2048),
+                       "model_over_T": model_ratio, "meas_over_f_base": m / f_base,
                        "alignment_limited": model_ratio < 0.9})
         L += ch
     r = np.array([cch["meas_over_T"] for cch in chunks])
     ok = np.array([not cch["alignment_limited"] for cch in chunks])
-    res = {"align": align, "fit": {"a": a, "b": bb, "c": c}, "T_ms": T,
+
+    # Online calibration of f(C, H) = a*C*(C+H) + b*(C+H) + c over the same prompt.
+    calib = cpa.Calib(min_points=5, window=30)
+    online = []
+    L = 0
+    while L < prompt:
+        try:
+            a2, b2, c2 = calib.model()
+            T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
+            ch, x = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
+            src = "online"
+        except cpa.CpaError:
+            ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
+            src = "profiled"
+        if ch <= 0:
+            break
+        m = median_ms(runner(L, ch), 11, 2)["median_ms"]
+        try:
+            calib.record(cpa.cpa_calib_features([ch], [L]), m)
+            refit = True
+        except cpa.CpaError:
+            refit = False   # window does not determine the model (e.g. one chunk size)
+        online.append({"L": L, "chunk": ch, "raw_x": x, "ms": m, "model": src, "refit": refit,
+                       "meas_over_f_base": m / f_base})
+        L += ch
+    try:
+        a2, b2, c2 = calib.model()
+    except cpa.CpaError:
+        a2 = b2 = c2 = None
+
+    res = {"shape": shape, "prompt": prompt, "align": align, "fit": {"a": a, "b": bb, "c": c},
+           "T_ms": T, "f_base_ms": f_base,
            "profile_ms": dict(zip(map(int, sizes), ms)), "num_chunks": len(chunks),
-           "meas_over_T": {"min": float(r.min()), "max": float(r.max()),
-                           "mean": float(r.mean()), "cv": float(r.std() / r.mean())},
+           "meas_over_T": summary(chunks, "meas_over_T"),
            "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1)),
            "frac_within_10pct_not_alignment_limited":
                float(np.mean(np.abs(r[ok] - 1) <= 0.1)) if ok.any() else None,
-           "chunks": chunks}
-    log(f"[bench] predictor align {align}: a={a:.3e} b={bb:.3e} c={c:.3e} T={T:.4f} ms, "
-        f"{len(chunks)} chunks, meas/T in [{r.min():.2f}, {r.max():.2f}]")
+           "meas_over_f_base": summary(chunks, "meas_over_f_base"),
+           "chunks": chunks,
+           "online": {"num_chunks": len(online), "final_fit": {"a": a2, "b": b2, "c": c2},
+                      "refused_refits": sum(1 for o in online if not o["refit"]),
+                      "meas_over_f_base": summary(online, "meas_over_f_base"),
+                      "chunks": online}}
+    log(f"[bench] predictor {shape} align {align}: a={a:.3e} b={bb:.3e} c={c:.3e} T={T:.4f} ms, "
+        f"{len(chunks)} chunks, meas/T in [{r.min():.2f}, {r.max():.2f}]; online: "
+        f"{len(online)} chunks, meas/f(base) cv {res['online']['meas_over_f_base']['cv']:.3f} "
+        f"vs {res['meas_over_f_base']['cv']:.3f}")
     return res
 
 
@@ -424,6 +478,7 @@ def main():
         out["long_context"] = long_context(args)
         out["predictor"] = predictor_run(args, 128)
         out["predictor_align16"] = predictor_run(args, 16)
+        out["predictor_llama3_8b"] = predictor_run(args, 128, shape="llama3_8b")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     out["context_from_pages"] = {

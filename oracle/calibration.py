@@ -22,6 +22,9 @@ Readings where the section is silent:
     are held, over the most recent window (30) records;
   * the columns are scaled by their largest magnitude in the window before
     the least-squares solve (a well-conditioned 3-column design);
+  * a window that does not determine three coefficients (e.g. one chunk
+    size throughout: C*(C+H) and C+H are then proportional, so a and b are
+    confounded) is not fitted; the previous model stays;
   * the per-chunk target is T' = f(base, 0) = a*base^2 + b*base + c, the
     modelled latency of a base-size chunk without history; the next chunk
     at history H solves f(C, H) = T', i.e.
@@ -69,7 +72,9 @@ def fit(feats, ms) -> tuple[float, float, float]:
     scale = np.max(np.abs(F), axis=0)
     if np.any(scale <= 0):
         raise ValueError("a feature column is all zero")
-    coef, *_ = np.linalg.lstsq(F / scale, t, rcond=None)
+    coef, _, rank, _ = np.linalg.lstsq(F / scale, t, rcond=None)
+    if rank < 3:
+        raise ValueError("records do not determine three coefficients")
     coef = coef / scale
     return float(coef[0]), float(coef[1]), float(coef[2])
 
@@ -132,5 +137,8 @@ class Calibrator:
         is available afterwards."""
         self.records.append((tuple(float(v) for v in feat), float(ms)))
         if len(self.records) >= self.min_points:
-            self.coef = fit([r[0] for r in self.records], [r[1] for r in self.records])
+            try:
+                self.coef = fit([r[0] for r in self.records], [r[1] for r in self.records])
+            except ValueError:
+                pass  # the window does not determine the model: keep the last one
         return self.coef is not None

@@ -281,3 +281,23 @@ def test_calib_rejects_bad_arguments(cpa):
     with pytest.raises(cpa.CpaError) as e:
         cpa.cpa_calib_features([5], [-1])
     assert e.value.status == cpa.CPA_ERR_INVALID_ARG
+
+
+def test_calib_rank_deficient_window(cpa):
+    from oracle.calibration import Calibrator, features
+    feats = [features([1024], [h]) for h in range(0, 10240, 1024)]
+    ms = [1e-7 * f[0] + 1e-3 * f[1] + 0.1 for f in feats]
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_calib_fit(feats, ms)
+    assert e.value.status == cpa.CPA_ERR_NUMERIC
+    h, ref = cpa.Calib(min_points=5, window=5), Calibrator(min_points=5, window=5)
+    for i, (f, m) in enumerate(zip(feats, ms)):
+        if i < 4:                      # fewer than min_points: no fit attempted
+            assert h.record(f, m) is False
+        else:                          # the fit is refused, no model yet
+            with pytest.raises(cpa.CpaError) as e:
+                h.record(f, m)
+            assert e.value.status == cpa.CPA_ERR_NUMERIC
+        assert ref.record(f, m) is False
+    with pytest.raises(cpa.CpaError):
+        h.model()

@@ -139,3 +139,21 @@ def test_calibrator_window_and_threshold():
     assert a == pytest.approx(2e-8, rel=1e-9)
     assert b == pytest.approx(4e-4, rel=1e-9)
     assert c == pytest.approx(0.05, rel=1e-9)
+
+
+def test_constant_chunk_size_does_not_determine_the_model():
+    # C fixed: C*(C+H) = C * (C+H), the first two columns are proportional.
+    feats = [cal.features([1024], [h]) for h in range(0, 10240, 1024)]
+    ms = [1e-7 * f[0] + 1e-3 * f[1] + 0.1 for f in feats]
+    with pytest.raises(ValueError):
+        cal.fit(feats, ms)
+    calib = cal.Calibrator(min_points=5, window=30)
+    good = [cal.features([c], [h]) for c, h in [(64, 0), (2048, 0), (512, 4096), (128, 9000), (1000, 20000)]]
+    for f in good:
+        calib.record(f, 2e-8 * f[0] + 3e-4 * f[1] + 0.02)
+    before = calib.coef
+    # a window holding only the constant-size records cannot be fitted
+    small = cal.Calibrator(min_points=5, window=5)
+    for f, m in zip(feats, ms):
+        assert small.record(f, m) is False
+    assert calib.coef == before
