@@ -187,6 +187,18 @@ def mixed_extras(args, mixed):
            "prefill_only_tflops": pf_flops / (r_pf["mean_ms"] * 1e-3) / 1e12}
     log(f"[bench] llama13b mixed call {res['mixed_call_us']:.1f} us; prefill chunks alone "
         f"{res['prefill_only_us']:.1f} us = {res['prefill_only_tflops']:.1f} TFLOP/s")
+    # Two micro-batches (dual-stream article, section 3.1) on two streams.
+    from chunked_prefill_attention_slot_amd.device import MicroBatchPair
+    for mode, name in ((cpa.CPA_SPLIT_BALANCED, "balanced"), (cpa.CPA_SPLIT_SIMPLE, "simple")):
+        split = cpa.cpa_split_point(b.query_lens, mode, 0.5, 64)
+        if split is None:
+            res[f"micro_batches_{name}"] = None
+            continue
+        pair = MicroBatchPair(db, *split)
+        r_mb = median_ms(pair.attention, args.decode_reps, 3)
+        res[f"micro_batches_{name}"] = {"split": list(split), "two_stream_us": r_mb["mean_ms"] * 1e3}
+        log(f"[bench] llama13b micro-batches ({name}, split {split}): two streams "
+            f"{r_mb['mean_ms'] * 1e3:.1f} us vs one call {res['mixed_call_us']:.1f} us")
     return res
 
 

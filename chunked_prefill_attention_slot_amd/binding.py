@@ -34,6 +34,7 @@ EXPORTS = (
     "cpa_predictor_fit", "cpa_predictor_target", "cpa_predictor_next_chunk",
     "cpa_calib_features", "cpa_calib_fit", "cpa_calib_target", "cpa_calib_next_chunk",
     "cpa_calib_create", "cpa_calib_destroy", "cpa_calib_record", "cpa_calib_model",
+    "cpa_split_point",
 )
 
 
@@ -118,6 +119,8 @@ _sig("cpa_calib_target", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg), ctyp
 _sig("cpa_calib_next_chunk", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
      ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
      ctypes.c_int64, _I64P, _F64P)
+_sig("cpa_split_point", ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+     ctypes.c_int32, _I32P, _I32P)
 _sig("cpa_calib_create", ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P))
 _sig("cpa_calib_destroy", ctypes.c_int32, _P)
 _sig("cpa_calib_record", ctypes.c_int32, _P, _F64P, ctypes.c_double, _I32P)
@@ -358,3 +361,19 @@ class Calib:
         _check(_lib.cpa_calib_model(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
                                     ctypes.byref(n)))
         return a.value, b.value, c.value
+
+
+# ---- two-micro-batch split ----
+
+CPA_SPLIT_SIMPLE, CPA_SPLIT_BALANCED = 0, 1
+
+
+def cpa_split_point(query_lens, mode: int = CPA_SPLIT_BALANCED, balance_threshold: float = 0.5,
+                    length_threshold: int = 1):
+    """(seq_split, token_split), or None when the split is refused."""
+    q = np.ascontiguousarray(query_lens, dtype=np.int32)
+    k, t = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.cpa_split_point(q.ctypes.data_as(_I32P), int(q.shape[0]), int(mode),
+                                float(balance_threshold), int(length_threshold),
+                                ctypes.byref(k), ctypes.byref(t)))
+    return None if k.value == 0 else (k.value, t.value)

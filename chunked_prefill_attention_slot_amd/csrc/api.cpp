@@ -501,3 +501,48 @@ cpa_status cpa_validate_metadata(const cpa_layer_desc* desc, const int32_t* slot
 }
 
 }  // extern "C"
+
+extern "C" cpa_status cpa_split_point(const int32_t* query_lens, int32_t num_seqs, int32_t mode,
+                                      double balance_threshold, int32_t length_threshold,
+                                      int32_t* seq_split, int32_t* token_split) {
+  if (!seq_split || !token_split || num_seqs < 0 || (num_seqs > 0 && !query_lens))
+    return cpa::fail(CPA_ERR_INVALID_ARG, "split_point: bad arguments");
+  *seq_split = 0;
+  *token_split = 0;
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (query_lens[s] < 0) return cpa::fail(CPA_ERR_INVALID_ARG, "split_point: negative query_len");
+    total += query_lens[s];
+  }
+  if (num_seqs < 2) return cpa::ok();  // no split
+  if (mode == CPA_SPLIT_SIMPLE) {
+    const int32_t k = num_seqs / 2;
+    int64_t tsp = 0;
+    for (int32_t s = 0; s < k; ++s) tsp += query_lens[s];
+    *seq_split = k;
+    *token_split = (int32_t)tsp;
+    return cpa::ok();
+  }
+  if (mode != CPA_SPLIT_BALANCED) return cpa::fail(CPA_ERR_INVALID_ARG, "split_point: unknown mode");
+  if (!(balance_threshold >= 0.0)) return cpa::fail(CPA_ERR_INVALID_ARG, "split_point: bad threshold");
+  const int64_t aim = total / 2;
+  int32_t best_k = 0;
+  int64_t best_c = 0, cumu = 0;
+  for (int32_t k = 1; k < num_seqs; ++k) {
+    cumu += query_lens[k - 1];
+    const int64_t d = cumu > aim ? cumu - aim : aim - cumu;
+    const int64_t db = best_c > aim ? best_c - aim : aim - best_c;
+    if (best_k == 0 || d < db) {
+      best_k = k;
+      best_c = cumu;
+    }
+  }
+  const int64_t n1 = best_c, n2 = total - best_c;
+  const int64_t lo = n1 < n2 ? n1 : n2, diff = n1 > n2 ? n1 - n2 : n2 - n1;
+  if (lo <= 0) return cpa::ok();
+  if ((double)diff / (double)lo > balance_threshold) return cpa::ok();
+  if (n1 < length_threshold || n2 < length_threshold) return cpa::ok();
+  *seq_split = best_k;
+  *token_split = (int32_t)best_c;
+  return cpa::ok();
+}

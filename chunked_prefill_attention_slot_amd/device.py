@@ -60,3 +60,37 @@ class DeviceBatch:
         if self.out.dtype == torch.float32:
             return self.out.cpu().numpy().astype(np.float64)
         return self.out.view(torch.bfloat16).to(torch.float64).cpu().numpy()
+
+
+class MicroBatchPair:
+    """A DeviceBatch split into two micro-batches at (seq_split,
+    token_split) (cpa_split_point): each half gets its own plan and
+    workspace, and attention() runs the halves on two streams, ordered after
+    the current stream's work and joined back into it. Marshalling only:
+    both halves are cpa_attention calls on row-offset views."""
+
+    def __init__(self, db: DeviceBatch, seq_split: int, token_split: int, options=None):
+        b = db.b
+        self.db = db
+        ql, sl = np.asarray(b.query_lens), np.asarray(b.seq_lens)
+        bounds = ((0, seq_split, 0, token_split),
+                  (seq_split, len(ql), token_split, int(b.num_tokens)))
+        self.parts = []
+        for s0, s1, t0, t1 in bounds:
+            plan = cpa.cpa_plan_create(db.desc, ql[s0:s1], sl[s0:s1], options)
+            ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+            cpa.cpa_plan_upload(plan, ws)
+            self.parts.append((plan, ws, s0, s1, t0, t1))
+        self.streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def attention(self):
+        db = self.db
+        cur = torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record(cur)
+        for (plan, ws, s0, s1, t0, t1), st in zip(self.parts, self.streams):
+            st.wait_event(ready)
+            cpa.cpa_attention(plan, db.q[t0:t1], db.k_cache, db.v_cache, db.block_table[s0:s1],
+                              db.out[t0:t1], ws, stream=st)
+        for st in self.streams:
+            cur.wait_stream(st)

@@ -254,6 +254,31 @@ cpa_status cpa_predictor_next_chunk(const cpa_predictor_cfg* cfg, double a,
                                     int64_t remaining, int64_t* chunk,
                                     double* raw_x);
 
+/* ---- Two-micro-batch split ([DS] section 3.1; host) ---- */
+
+enum { CPA_SPLIT_SIMPLE = 0, CPA_SPLIT_BALANCED = 1 };
+
+/*
+ * Split point of a flattened batch into two micro-batches ([DS] section
+ * 3.1 "data split"). CPA_SPLIT_SIMPLE: seq_split = num_seqs / 2.
+ * CPA_SPLIT_BALANCED: the boundary k in 1 .. num_seqs-1 whose running token
+ * count sum(query_lens[:k]) is nearest total/2 (ties to the smaller k); the
+ * split is refused when |n1 - n2| / min(n1, n2) > balance_threshold, or
+ * either micro-batch has fewer than length_threshold tokens, or one of them
+ * is empty. token_split = sum(query_lens[:seq_split]). A refused split (or
+ * num_seqs < 2) returns CPA_OK with *seq_split = *token_split = 0.
+ *
+ * The micro-batches are then: sequences [0, seq_split) and [seq_split,
+ * num_seqs) (query_lens, seq_lens, block_table rows), tokens [0,
+ * token_split) and [token_split, num_tokens) (q, out, k_new, v_new,
+ * slot_mapping rows). Each half is planned with cpa_plan_create on its own
+ * lengths and run with cpa_attention on pointers offset by those rows, in
+ * its own workspace; halves on two streams may run concurrently.
+ */
+cpa_status cpa_split_point(const int32_t* query_lens, int32_t num_seqs, int32_t mode,
+                           double balance_threshold, int32_t length_threshold,
+                           int32_t* seq_split, int32_t* token_split);
+
 /* ---- Online calibration ([CPP] "online calibration"; host fp64) ---- */
 
 /*

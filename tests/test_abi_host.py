@@ -301,3 +301,23 @@ def test_calib_rank_deficient_window(cpa):
         assert ref.record(f, m) is False
     with pytest.raises(cpa.CpaError):
         h.model()
+
+
+# ---- two-micro-batch split: C++ vs oracle --------------------------------------
+
+def test_split_point_matches_oracle(cpa):
+    from oracle.split import balanced_split, simple_split
+    rng = np.random.default_rng(21)
+    cases = [[1] * 16 + [512, 512], [5], [], [0, 0], [3, 2, 3], [2, 2, 2, 2]]
+    cases += [[int(v) for v in rng.integers(0, 700, int(rng.integers(1, 15)))] for _ in range(300)]
+    for ql in cases:
+        assert cpa.cpa_split_point(ql, cpa.CPA_SPLIT_SIMPLE) == simple_split(ql)
+        for bt, lt in [(0.5, 1), (0.05, 100), (3.0, 0), (0.0, 1)]:
+            assert cpa.cpa_split_point(ql, cpa.CPA_SPLIT_BALANCED, bt, lt) == balanced_split(ql, bt, lt), (ql, bt, lt)
+
+
+def test_split_point_rejects_bad_arguments(cpa):
+    for args in [([1, -2], 0, 0.5, 1), ([1, 2], 7, 0.5, 1), ([1, 2], 1, float("nan"), 1)]:
+        with pytest.raises(cpa.CpaError) as e:
+            cpa.cpa_split_point(*args)
+        assert e.value.status == cpa.CPA_ERR_INVALID_ARG

@@ -176,6 +176,50 @@ def test_llama13b_mixed_batch(H):
     run_and_compare(H, b, "llama13b mixed", rows=rows)
 
 
+def _run_micro_batches(H, b, label, mode, rows=None):
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.device import MicroBatchPair
+    split = cpa.cpa_split_point(b.query_lens, mode, 0.5, 1)
+    assert split is not None
+    banner(f"{label}: micro-batches at {split}")
+    whole = H.DeviceBatch(b)
+    whole.run()
+    db = H.DeviceBatch(b)
+    db.kv_write()
+    pair = MicroBatchPair(db, *split)
+    pair.attention()
+    torch.cuda.synchronize()
+    got = db.out_f64()
+    ref = H.oracle_out(b, rows=rows)
+    H.compare(got, ref, label)
+    # and the two halves agree with the one-call output on every row
+    H.compare(got, whole.out_f64(), label + " vs one call")
+    return split
+
+
+def test_micro_batch_split_small(H):
+    """Decode rows then prefill chunks (the chunked-prefill article's token
+    budget order), split in two by the balanced rule of the dual-stream
+    article and run on two streams."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    b = make(seed=31, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+             query_lens=[1, 1, 1, 1, 90, 70], seq_lens=[300, 17, 129, 64, 200, 70], extra_pages=4)
+    split = _run_micro_batches(H, b, "micro-batches balanced", cpa.CPA_SPLIT_BALANCED)
+    assert split == (5, 94)
+    _run_micro_batches(H, b, "micro-batches simple", cpa.CPA_SPLIT_SIMPLE)
+
+
+def test_micro_batch_split_llama13b(H):
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import mixed_llama13b
+    b = mixed_llama13b()
+    rows = {s: [0] for s in range(16)}
+    rows[16] = sample_rows(512, 8, 3)
+    rows[17] = sample_rows(512, 8, 4)
+    split = _run_micro_batches(H, b, "llama13b micro-batches", cpa.CPA_SPLIT_BALANCED, rows=rows)
+    assert split == (17, 528)
+
+
 @pytest.mark.parametrize("hist", [0, 30720])
 def test_long_context_chunk2048(H, hist):
     """64 q / 8 kv heads, d=128, C=2048 at prefix H (max_model_len 32768)."""
