@@ -34,7 +34,8 @@ EXPORTS = (
     "cpa_predictor_fit", "cpa_predictor_target", "cpa_predictor_next_chunk",
     "cpa_calib_features", "cpa_calib_fit", "cpa_calib_target", "cpa_calib_next_chunk",
     "cpa_calib_create", "cpa_calib_destroy", "cpa_calib_record", "cpa_calib_model",
-    "cpa_split_point",
+    "cpa_split_point", "cpa_sched_create", "cpa_sched_destroy", "cpa_sched_add",
+    "cpa_sched_set_model", "cpa_sched_form", "cpa_sched_commit", "cpa_sched_status",
 )
 
 
@@ -76,6 +77,14 @@ class cpa_predictor_cfg(ctypes.Structure):
     _fields_ = [("base_chunk_size", ctypes.c_int64), ("align", ctypes.c_int64),
                 ("min_chunk", ctypes.c_int64), ("max_chunk", ctypes.c_int64),
                 ("max_model_len", ctypes.c_int64), ("smooth_factor", ctypes.c_double)]
+
+
+class cpa_sched_cfg(ctypes.Structure):
+    _fields_ = [("budget", ctypes.c_int32), ("rule", ctypes.c_int32),
+                ("fixed_chunk", ctypes.c_int32), ("num_sizes", ctypes.c_int32),
+                ("sizes", ctypes.c_int32 * 8), ("pred", cpa_predictor_cfg),
+                ("a", ctypes.c_double), ("b", ctypes.c_double), ("c", ctypes.c_double),
+                ("T", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -121,6 +130,14 @@ _sig("cpa_calib_next_chunk", ctypes.c_int32, ctypes.POINTER(cpa_predictor_cfg),
      ctypes.c_int64, _I64P, _F64P)
 _sig("cpa_split_point", ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
      ctypes.c_int32, _I32P, _I32P)
+_sig("cpa_sched_create", ctypes.c_int32, ctypes.POINTER(cpa_sched_cfg), ctypes.POINTER(_P))
+_sig("cpa_sched_destroy", ctypes.c_int32, _P)
+_sig("cpa_sched_add", ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P)
+_sig("cpa_sched_set_model", ctypes.c_int32, _P, ctypes.c_double, ctypes.c_double,
+     ctypes.c_double, ctypes.c_double)
+_sig("cpa_sched_form", ctypes.c_int32, _P, ctypes.c_int32, _I32P, _I32P, _I32P, _I32P)
+_sig("cpa_sched_commit", ctypes.c_int32, _P)
+_sig("cpa_sched_status", ctypes.c_int32, _P, _I32P, _I32P)
 _sig("cpa_calib_create", ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P))
 _sig("cpa_calib_destroy", ctypes.c_int32, _P)
 _sig("cpa_calib_record", ctypes.c_int32, _P, _F64P, ctypes.c_double, _I32P)
@@ -377,3 +394,59 @@ def cpa_split_point(query_lens, mode: int = CPA_SPLIT_BALANCED, balance_threshol
                                 float(balance_threshold), int(length_threshold),
                                 ctypes.byref(k), ctypes.byref(t)))
     return None if k.value == 0 else (k.value, t.value)
+
+
+# ---- token-budget batch former ----
+
+CPA_RULE_FIXED, CPA_RULE_PROGRESSIVE, CPA_RULE_PREDICTOR, CPA_RULE_CALIBRATED = 0, 1, 2, 3
+
+
+def sched_cfg(budget: int, rule: int = CPA_RULE_FIXED, fixed_chunk: int = 512, sizes=(),
+              pred=None, a=0.0, b=0.0, c=0.0, T=0.0) -> cpa_sched_cfg:
+    cfg = cpa_sched_cfg()
+    cfg.budget, cfg.rule, cfg.fixed_chunk = int(budget), int(rule), int(fixed_chunk)
+    cfg.num_sizes = len(sizes)
+    for i, v in enumerate(sizes):
+        cfg.sizes[i] = int(v)
+    cfg.pred = pred if pred is not None else predictor_cfg()
+    cfg.a, cfg.b, cfg.c, cfg.T = float(a), float(b), float(c), float(T)
+    return cfg
+
+
+class Sched:
+    """Owns a cpa_sched (cpa_sched_create / _destroy)."""
+
+    def __init__(self, cfg: cpa_sched_cfg):
+        h = _P()
+        _check(_lib.cpa_sched_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib.cpa_sched_destroy(self._h)
+            self._h = None
+
+    def add(self, prompt_len: int, max_new: int, arrival: int = 0) -> int:
+        rid = ctypes.c_int32()
+        _check(_lib.cpa_sched_add(self._h, int(prompt_len), int(max_new), int(arrival),
+                                  ctypes.byref(rid)))
+        return rid.value
+
+    def set_model(self, a: float, b: float, c: float, T: float):
+        _check(_lib.cpa_sched_set_model(self._h, a, b, c, T))
+
+    def form(self, capacity: int = 4096):
+        ids = (ctypes.c_int32 * capacity)()
+        ql = (ctypes.c_int32 * capacity)()
+        sl = (ctypes.c_int32 * capacity)()
+        n = ctypes.c_int32()
+        _check(_lib.cpa_sched_form(self._h, capacity, ids, ql, sl, ctypes.byref(n)))
+        return [(ids[i], ql[i], sl[i]) for i in range(n.value)]
+
+    def commit(self):
+        _check(_lib.cpa_sched_commit(self._h))
+
+    def status(self):
+        f, st = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.cpa_sched_status(self._h, ctypes.byref(f), ctypes.byref(st)))
+        return bool(f.value), st.value

@@ -351,6 +351,61 @@ cpa_status cpa_calib_record(cpa_calib calib, const double* feat, double ms,
 cpa_status cpa_calib_model(cpa_calib calib, double* a, double* b, double* c,
                            int32_t* points);
 
+/* ---- Token-budget batch former ([CP] section 3.1; host) ---- */
+
+enum {
+  CPA_RULE_FIXED = 0,        /* chunk cap = fixed_chunk ([CP] 3.1: typically 512) */
+  CPA_RULE_PROGRESSIVE = 1,  /* k-th chunk of a request capped by sizes[min(k, n-1)] ([CP] 3.2.2) */
+  CPA_RULE_PREDICTOR = 2,    /* cpa_predictor_next_chunk(pred, a, b, T, L, remaining) ([CPP]) */
+  CPA_RULE_CALIBRATED = 3    /* cpa_calib_next_chunk(pred, a, b, c, T, L, remaining) ([CPP]) */
+};
+
+typedef struct cpa_sched_cfg {
+  int32_t budget;           /* tokens per step (> 0) */
+  int32_t rule;             /* CPA_RULE_* */
+  int32_t fixed_chunk;      /* CPA_RULE_FIXED */
+  int32_t num_sizes;        /* CPA_RULE_PROGRESSIVE: 1..8 */
+  int32_t sizes[8];
+  cpa_predictor_cfg pred;   /* predictor / calibrated rules */
+  double a, b, c, T;        /* model coefficients and target of those rules */
+} cpa_sched_cfg;
+
+typedef struct cpa_sched_s* cpa_sched;
+cpa_status cpa_sched_create(const cpa_sched_cfg* cfg, cpa_sched* out);
+cpa_status cpa_sched_destroy(cpa_sched sched);
+
+/* A request of prompt_len > 0 tokens generating max_new >= 0 tokens after
+ * its prompt, admissible from step arrival_step on. Ids count from 0. */
+cpa_status cpa_sched_add(cpa_sched sched, int32_t prompt_len, int32_t max_new,
+                         int32_t arrival_step, int32_t* request_id);
+
+/* New model coefficients for the predictor / calibrated rules (e.g. from
+ * cpa_calib_model and cpa_calib_target); used from the next formed batch. */
+cpa_status cpa_sched_set_model(cpa_sched sched, double a, double b, double c, double T);
+
+/*
+ * Forms the current step's batch within the budget ([CP] 3.1): first one
+ * decode row per admitted request whose prompt is prefilled (query_len 1,
+ * seq_len = prompt_len + generated + 1), then one chunk per unfinished
+ * prefill, chunk = min(remaining prompt, budget left, rule cap at prefix L),
+ * then, if the unfinished prefills did not exhaust the budget, new requests
+ * in arrival order (ties by id) while budget is left. Decode rows and
+ * unfinished prefills are visited in admission order. A request whose
+ * prompt completes becomes a decode row from the next step; it finishes
+ * after max_new decode rows. Writes up to `capacity` entries (request id,
+ * query_len, seq_len, in flattened-axis order) and *num_seqs;
+ * CPA_ERR_INVALID_ARG (state unchanged, *num_seqs = the size needed) when
+ * capacity is too small. Call cpa_sched_commit after running the batch.
+ */
+cpa_status cpa_sched_form(cpa_sched sched, int32_t capacity, int32_t* request_ids,
+                          int32_t* query_lens, int32_t* seq_lens, int32_t* num_seqs);
+
+/* Advances the requests by the formed batch and the step counter. */
+cpa_status cpa_sched_commit(cpa_sched sched);
+
+/* *finished = 1 once every request is done; *step = steps committed. */
+cpa_status cpa_sched_status(cpa_sched sched, int32_t* finished, int32_t* step);
+
 #ifdef __cplusplus
 }
 #endif

@@ -321,3 +321,59 @@ def test_split_point_rejects_bad_arguments(cpa):
         with pytest.raises(cpa.CpaError) as e:
             cpa.cpa_split_point(*args)
         assert e.value.status == cpa.CPA_ERR_INVALID_ARG
+
+
+# ---- token-budget batch former: C++ vs oracle ----------------------------------
+
+def _both_schedulers(cpa, budget, kind, seed):
+    from oracle import predictor as P
+    from oracle import scheduler as S
+    a, b, c = 1.1e-7, 7e-4, 0.05
+    ocfg = P.PredictorConfig(align=16)
+    if kind == S.RULE_CALIBRATED:
+        from oracle.calibration import target as t2
+        T = t2(a, b, c, 2048)
+    else:
+        T = P.target(a, b, 2048)
+    rule = S.Rule(kind, fixed=384, sizes=(2048, 1024, 512), cfg=ocfg, a=a, b=b, c=c, T=T)
+    cc = cpa.sched_cfg(budget, kind, fixed_chunk=384, sizes=(2048, 1024, 512),
+                       pred=cpa.predictor_cfg(align=16), a=a, b=b, c=c, T=T)
+    return S.Scheduler(budget, rule), cpa.Sched(cc)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("seed", range(4))
+def test_scheduler_matches_oracle(cpa, kind, seed):
+    rng = np.random.default_rng(100 * kind + seed)
+    budget = int(rng.choice([128, 512, 2048]))
+    ref, got = _both_schedulers(cpa, budget, kind, seed)
+    for _ in range(int(rng.integers(1, 16))):
+        p, m, t = int(rng.integers(1, 9000)), int(rng.integers(0, 40)), int(rng.integers(0, 50))
+        assert ref.add(p, m, t) == got.add(p, m, t)
+    steps = 0
+    while not ref.finished():
+        assert got.form() == ref.form()
+        ref.commit()
+        got.commit()
+        steps += 1
+        assert got.status() == (ref.finished(), steps)
+    assert got.status()[0]
+
+
+def test_scheduler_capacity_and_protocol(cpa):
+    s = cpa.Sched(cpa.sched_cfg(1 << 20, cpa.CPA_RULE_FIXED, fixed_chunk=1 << 20))
+    for p in (5, 6, 7):
+        s.add(p, 1)
+    with pytest.raises(cpa.CpaError):
+        s.form(capacity=2)                       # three sequences do not fit
+    assert s.form(capacity=3) == [(0, 5, 5), (1, 6, 6), (2, 7, 7)]
+    with pytest.raises(cpa.CpaError):
+        s.form()                                 # commit first
+    s.commit()
+    assert s.form() == [(0, 1, 6), (1, 1, 7), (2, 1, 8)]
+    s.commit()
+    assert s.status() == (True, 2)
+    with pytest.raises(cpa.CpaError):
+        cpa.Sched(cpa.sched_cfg(0))
+    with pytest.raises(cpa.CpaError):
+        cpa.Sched(cpa.sched_cfg(64, cpa.CPA_RULE_PROGRESSIVE, sizes=()))
