@@ -20,8 +20,10 @@ The printed JSON line (last line of stdout) carries:
   decode     -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
                 40/40 heads): algorithmic K+V+Q+O bytes / time vs HBM peak;
   cpu_baseline -- the fp64 oracle on a bounded sample of the H=12288 chunk.
---extras adds the mixed batch, the 70B-like long-context sweep and the
-chunk-size predictor run as extra fields.
+--extras adds the mixed batch, the 70B-like long-context sweep, the
+chunk-size predictor runs, the token-budget step loop under four chunk
+rules and the chunk-size sweep around 512 as extra fields (--serving adds
+only the last two).
 """
 from __future__ import annotations
 
@@ -246,6 +248,34 @@ PREDICTOR_SHAPES = {
 }
 
 
+def chunk_runner(db, cpa, torch):
+    """runner(L, c) -> a closure doing KV write + attention of the chunk
+    [L, L + c) of db's single sequence."""
+    def runner(L, c):
+        plan = cpa.cpa_plan_create(db.desc, [c], [L + c])
+        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+        cpa.cpa_plan_upload(plan, ws)
+        sl = slice(L, L + c)
+        kn, vn, sm, q, out = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl], db.q[sl], db.out[sl]
+
+        def f():
+            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
+            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+        f.plan = plan
+        return f
+    return runner
+
+
+def profile_fit(runner):
+    """Startup profiling (dynamic-chunking design, "startup"): median ms of
+    KV write + attention for a fresh chunk of each of the 64 sizes 2048,
+    2016, .., 32, and the least-squares quadratic through them."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    sizes = cpa.cpa_predictor_profile_sizes(2048, 64, 32)
+    ms = [median_ms(runner(0, l), 21, 3)["median_ms"] for l in sizes]
+    return sizes, ms, cpa.cpa_predictor_fit(sizes, ms)
+
+
 def predictor_run(args, align=128, shape="tiny", prompt=32768):
     """Startup profiling at 64 sizes (2048 down to 32, H=0) of KV write +
     attention, least-squares fit, target T = f(2048) - f(0), then a prompt
@@ -259,22 +289,9 @@ def predictor_run(args, align=128, shape="tiny", prompt=32768):
     from chunked_prefill_attention_slot_amd.device import DeviceBatch
     b = make_batch(3, query_lens=[prompt], seq_lens=[prompt], **PREDICTOR_SHAPES[shape])
     db = DeviceBatch(b)
+    runner = chunk_runner(db, cpa, torch)
 
-    def runner(L, c):
-        plan = cpa.cpa_plan_create(db.desc, [c], [L + c])
-        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
-        cpa.cpa_plan_upload(plan, ws)
-        sl = slice(L, L + c)
-        kn, vn, sm, q, out = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl], db.q[sl], db.out[sl]
-
-        def f():
-            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
-            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
-        return f
-
-    sizes = cpa.cpa_predictor_profile_sizes(2048, 64, 32)
-    ms = [median_ms(runner(0, l), 21, 3)["median_ms"] for l in sizes]
-    a, bb, c = cpa.cpa_predictor_fit(sizes, ms)
+    sizes, ms, (a, bb, c) = profile_fit(runner)
     cfg = cpa.predictor_cfg(align=align)
     T = cpa.cpa_predictor_target(cfg, a, bb)
     f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c   # modelled latency of a base chunk at H=0
@@ -350,6 +367,196 @@ def predictor_run(args, align=128, shape="tiny", prompt=32768):
         f"{len(online)} chunks, meas/f(base) cv {res['online']['meas_over_f_base']['cv']:.3f} "
         f"vs {res['meas_over_f_base']['cv']:.3f}")
     return res
+
+
+LLAMA3_8B = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128)
+
+
+def step_loop(requests, budget, rule, fit, seed=7, align=128):
+    """One pass of the token-budget step loop (vLLM chunked-prefill article,
+    section 3.1) over a request stream at the Llama-3-8B layer: libcpa's
+    batch former forms each step, the stream lays out its metadata, and the
+    step's KV write + attention run on one cache kept across steps. Each
+    step's GPU time comes from events around its two calls, after which the
+    host waits for the step (so host work is outside the figure). rule is
+    ("fixed", size) | ("progressive", sizes) | ("predictor",) |
+    ("calibrated",): the last refits f(C, H) online from every step's
+    features and time and hands the model to the former."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.device import ServingCaches
+    from chunked_prefill_attention_slot_amd.inputs import ServingStream
+    a, b, c = fit
+    pcfg = cpa.predictor_cfg(align=align)
+    kind = rule[0]
+    if kind == "fixed":
+        cfg = cpa.sched_cfg(budget, cpa.CPA_RULE_FIXED, fixed_chunk=rule[1])
+    elif kind == "progressive":
+        cfg = cpa.sched_cfg(budget, cpa.CPA_RULE_PROGRESSIVE, sizes=rule[1])
+    elif kind == "predictor":
+        cfg = cpa.sched_cfg(budget, cpa.CPA_RULE_PREDICTOR, pred=pcfg, a=a, b=b,
+                            T=cpa.cpa_predictor_target(pcfg, a, b))
+    else:   # the one-variable fit is f(C, 0) of the two-variable model until refits exist
+        cfg = cpa.sched_cfg(budget, cpa.CPA_RULE_CALIBRATED, pred=pcfg, a=a, b=b, c=c,
+                            T=cpa.cpa_calib_target(pcfg, a, b, c))
+    sched = cpa.Sched(cfg)
+    for p, m, t in requests:
+        sched.add(p, m, t)
+    calib = cpa.Calib(min_points=5, window=30) if kind == "calibrated" else None
+    stream = ServingStream(seed, requests=requests, **LLAMA3_8B)
+    dev = ServingCaches(stream, init="zeros")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    hq, hkv, d = LLAMA3_8B["num_q_heads"], LLAMA3_8B["num_kv_heads"], LLAMA3_8B["head_dim"]
+
+    def pool(h):
+        return torch.randn((budget, h, d), generator=g, device="cuda").to(torch.bfloat16) \
+            .view(torch.int16)
+    pools = (pool(hq), pool(hkv), pool(hkv))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps, refused, host_s = [], 0, 0.0
+    first_tok, dec_times = {}, {}
+    cum = 0.0
+    while True:
+        done, step_no = sched.status()
+        if done:
+            break
+        h0 = time.perf_counter()
+        batch = sched.form()
+        st = stream.step(batch, draw=False)
+        dev.load(st, *pools)
+        host_s += time.perf_counter() - h0
+        if step_no == 0:                      # warm the kernels on the first step's shapes
+            for _ in range(2):
+                dev.kv_write()
+                dev.attention()
+        e0.record()
+        dev.kv_write()
+        dev.attention()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) if st.num_tokens else 0.0
+        start, cum = cum, cum + ms
+        n_dec = 0
+        for rid, q, n in batch:
+            p, _, arr = requests[rid]
+            if n > p:
+                n_dec += 1
+                dec_times.setdefault(rid, []).append(cum)
+            elif n == p:
+                first_tok[rid] = (arr, cum)
+        steps.append({"tokens": st.num_tokens, "rows": len(batch), "decode_rows": n_dec,
+                      "ms": ms, "start_ms": start})
+        if calib is not None and st.num_tokens:
+            try:
+                calib.record(cpa.cpa_calib_features(st.query_lens, st.seq_lens - st.query_lens),
+                             ms)
+            except cpa.CpaError:
+                refused += 1
+            try:
+                a2, b2, c2 = calib.model()
+                sched.set_model(a2, b2, c2, cpa.cpa_calib_target(pcfg, a2, b2, c2))
+            except cpa.CpaError:
+                pass
+        sched.commit()
+    # time to first token: from the start of the arrival step to the end of
+    # the step that finishes the prompt; inter-token gaps between a request's
+    # token-producing steps
+    start_of = [s["start_ms"] for s in steps]
+    ttft = [end - start_of[min(arr, len(start_of) - 1)] for arr, end in first_tok.values()]
+    itl = []
+    for rid, ts in dec_times.items():
+        prev = first_tok[rid][1]
+        for t in ts:
+            itl.append(t - prev)
+            prev = t
+    busy_idx = [i for i, s in enumerate(steps) if s["tokens"] > s["decode_rows"]]  # with prefill
+    busy = [steps[i]["ms"] for i in busy_idx]
+
+    def stats(v):
+        v = np.asarray(v, dtype=np.float64)
+        if v.size == 0:
+            return None
+        return {"mean": float(v.mean()), "p50": float(np.percentile(v, 50)),
+                "p90": float(np.percentile(v, 90)), "max": float(v.max()),
+                "cv": float(v.std() / v.mean()) if v.mean() > 0 else 0.0}
+    tot = sum(s["ms"] for s in steps)
+    ntok = sum(s["tokens"] for s in steps)
+    res = {"rule": list(rule) if len(rule) > 1 else [kind], "steps": len(steps),
+           "gpu_ms_total": tot, "tokens": ntok,
+           "prefill_chunks": sum(s["rows"] - s["decode_rows"] for s in steps),
+           "tokens_per_s": ntok / (tot * 1e-3) if tot else None,
+           "step_ms_with_prefill": stats(busy),
+           "slowest_step": (lambda i: {"index": i, **steps[i]})(max(busy_idx, key=lambda i:
+                                                                       steps[i]["ms"]))
+           if busy_idx else None,
+           "ttft_ms": stats(ttft), "itl_ms": stats(itl),
+           "host_ms_per_step": host_s * 1e3 / max(1, len(steps))}
+    if calib is not None:
+        res["refused_refits"] = refused
+        try:
+            res["final_model"] = list(calib.model())
+        except cpa.CpaError:
+            res["final_model"] = None
+    return res
+
+
+def serving_run(args):
+    """The step loop at the Llama-3-8B layer under four chunk rules, on a
+    seeded stream of 16 requests (budget 2048) and on one 32768-token prompt
+    alone (the chunk-schedule comparison: fixed 512, progressive
+    [2048, 1024, 512], predictor-sized, calibrated). The predictor rules use
+    a fit profiled at this layer at startup."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_request_stream, make_batch
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+    b = make_batch(3, query_lens=[2048], seq_lens=[2048], **LLAMA3_8B)
+    db = DeviceBatch(b)
+    sizes, ms, fit = profile_fit(chunk_runner(db, cpa, torch))
+    del db
+    rules = [("fixed", 512), ("progressive", (2048, 1024, 512)), ("predictor",), ("calibrated",)]
+    out = {"fit": list(fit), "budget": 2048}
+    for name, reqs in (("stream16", llama3_8b_request_stream()), ("single32k", [(32768, 0, 0)])):
+        rows = []
+        for rule in rules:
+            r = step_loop(reqs, 2048, rule, fit)
+            rows.append(r)
+            bs = r["step_ms_with_prefill"]
+            log(f"[bench] step loop {name} {r['rule']}: {r['steps']} steps, {r['gpu_ms_total']:.1f} "
+                f"ms GPU, {r['prefill_chunks']} chunks, prefill-step ms mean {bs['mean']:.3f} "
+                f"p90 {bs['p90']:.3f} max {bs['max']:.3f} cv {bs['cv']:.3f}"
+                + (f", ttft mean {r['ttft_ms']['mean']:.1f} ms" if r["ttft_ms"] else "")
+                + (f", itl p90 {r['itl_ms']['p90']:.3f} ms" if r["itl_ms"] else ""))
+            torch.cuda.empty_cache()
+        out[name] = {"requests": len(reqs), "prompt_tokens": sum(p for p, _, _ in reqs),
+                     "decode_tokens": sum(m for _, m, _ in reqs), "rules": rows}
+    return out
+
+
+def alignment_study(args, hists=(0, 4096, 12288),
+                    sizes=(384, 448, 496, 511, 512, 513, 528, 544, 576, 640)):
+    """Chunk-size sweep around 512 at the Llama-3-8B layer (KV write +
+    attention of one chunk at prefix H): the cost of a chunk one token past a
+    tile multiple, which the vLLM chunked-prefill article prices at +32%
+    for 512 -> 513 on its GPU."""
+    import torch
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+    n = max(hists) + max(sizes)
+    b = make_batch(6, query_lens=[n], seq_lens=[n], **LLAMA3_8B)
+    db = DeviceBatch(b)
+    db.kv_write()
+    run = chunk_runner(db, cpa, torch)
+    out = {}
+    for h in hists:
+        row = {int(c): median_ms(run(h, c), 31, 3)["median_ms"] * 1e3 for c in sizes}
+        out[str(h)] = {"us": row, "ratio_513_over_512": row[513] / row[512],
+                       "ratio_511_over_512": row[511] / row[512]}
+        log(f"[bench] alignment H={h}: " + " ".join(f"{c}:{u:.1f}" for c, u in row.items())
+            + f" us; 513/512 = {row[513] / row[512]:.3f}")
+    return out
 
 
 def cpu_baseline(budget_s=10.0):
@@ -437,6 +644,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--hist", type=int, nargs="+", default=list(HIST_SWEEP),
                     help="prefixes of the headline sweep (profiling subsets)")
+    ap.add_argument("--serving", action="store_true",
+                    help="add the step-loop and chunk-alignment legs (also part of --extras)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -491,6 +700,9 @@ def main():
         out["predictor"] = predictor_run(args, 128)
         out["predictor_align16"] = predictor_run(args, 16)
         out["predictor_llama3_8b"] = predictor_run(args, 128, shape="llama3_8b")
+    if args.extras or args.serving:
+        out["step_loop"] = serving_run(args)
+        out["alignment"] = alignment_study(args)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     out["context_from_pages"] = {

@@ -94,3 +94,66 @@ class MicroBatchPair:
                               db.out[t0:t1], ws, stream=st)
         for st in self.streams:
             cur.wait_stream(st)
+
+
+class ServingCaches:
+    """Device K/V caches of a ServingStream's page pool, kept across steps,
+    and the marshalling of one step: upload its metadata (and tokens), build
+    and upload its plan, then KV write and attention through libcpa.
+    `init="sentinel"` copies the stream's sentinel-filled caches to the
+    device; `init="zeros"` only allocates and zeroes them (the content of a
+    slot is never read before the step that writes it)."""
+
+    def __init__(self, stream, out_dtype=cpa.CPA_DTYPE_BF16, options=None, init="sentinel"):
+        self.stream = stream
+        self.options = options
+        self.out_dtype = out_dtype
+        self.desc = cpa.layer_desc(stream.num_q_heads, stream.num_kv_heads, stream.head_dim,
+                                   stream.page_size, stream.num_blocks,
+                                   stream.max_blocks_per_seq, out_dtype=out_dtype)
+        if init == "sentinel":
+            kc, vc = stream.initial_caches()
+            self.k_cache, self.v_cache = to_dev_u16(kc), to_dev_u16(vc)
+        else:
+            shape = (stream.num_blocks, stream.num_kv_heads, stream.page_size, stream.head_dim)
+            self.k_cache = torch.zeros(shape, dtype=torch.int16, device="cuda")
+            self.v_cache = torch.zeros(shape, dtype=torch.int16, device="cuda")
+        self.workspace = torch.empty(256, dtype=torch.uint8, device="cuda")
+        self.num_tokens = 0
+
+    def load(self, st, q=None, k_new=None, v_new=None):
+        """Take one step's StepInputs. Token tensors default to the drawn
+        ones in `st`; device tensors of at least the step's token count may
+        be passed instead (their leading rows are used)."""
+        T = st.num_tokens
+        self.num_tokens = T
+        if T == 0:
+            return
+        self.q = q[:T] if q is not None else to_dev_u16(st.q)
+        self.k_new = k_new[:T] if k_new is not None else to_dev_u16(st.k_new)
+        self.v_new = v_new[:T] if v_new is not None else to_dev_u16(st.v_new)
+        self.slot_mapping = to_dev_i32(st.slot_mapping)
+        self.block_table = to_dev_i32(st.block_table)
+        self.plan = cpa.cpa_plan_create(self.desc, st.query_lens, st.seq_lens, self.options)
+        if self.plan.workspace_bytes > self.workspace.numel():
+            self.workspace = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8,
+                                         device="cuda")
+        cpa.cpa_plan_upload(self.plan, self.workspace)
+        dt = torch.float32 if self.out_dtype == cpa.CPA_DTYPE_F32 else torch.int16
+        self.out = torch.empty((T, self.stream.num_q_heads, self.stream.head_dim), dtype=dt,
+                               device="cuda")
+
+    def kv_write(self):
+        if self.num_tokens:
+            cpa.cpa_kv_write(self.desc, self.k_new, self.v_new, self.slot_mapping,
+                             self.k_cache, self.v_cache)
+
+    def attention(self):
+        if self.num_tokens:
+            cpa.cpa_attention(self.plan, self.q, self.k_cache, self.v_cache, self.block_table,
+                              self.out, self.workspace)
+
+    def out_f64(self) -> np.ndarray:
+        if self.out.dtype == torch.float32:
+            return self.out.cpu().numpy().astype(np.float64)
+        return self.out.view(torch.bfloat16).to(torch.float64).cpu().numpy()

@@ -209,3 +209,96 @@ def long_context_chunk(hist: int, seed: int = 5, chunk: int = 2048,
                       page_size=128, query_lens=[chunk],
                       seq_lens=[hist + chunk],
                       max_blocks_per_seq=math.ceil(max_model_len / 128))
+
+
+# --- A request stream over many steps -----------------------------------
+# The token-budget step loop (vLLM chunked-prefill article, section 3.1)
+# prefills each prompt over several steps and then decodes one token per
+# step, all into one paged cache. ServingStream fixes each request's pages
+# up front and, for every formed batch, lays out that step's flattened
+# metadata and draws its new tokens.
+
+@dataclass
+class StepInputs:
+    query_lens: np.ndarray        # [S] int32
+    seq_lens: np.ndarray          # [S] int32
+    block_table: np.ndarray       # [S, max_blocks] int32, -1 past a request's pages
+    slot_mapping: np.ndarray      # [T] int32
+    q: np.ndarray | None          # [T, Hq, d] bf16 bits (None when not drawn)
+    k_new: np.ndarray | None      # [T, Hkv, d]
+    v_new: np.ndarray | None
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_lens.sum())
+
+
+class ServingStream:
+    """Seeded pages and per-step tokens for a stream of requests.
+
+    requests: (prompt_len, max_new, arrival_step) triples. Request r owns
+    ceil((prompt_len + max_new) / page_size) pages, taken in order from a
+    seeded permutation of a pool of that many pages plus `extra_pages`; its
+    token at absolute position p goes to slot page[p // P] * P + p % P.
+    `step(batch)` takes a formed batch, a list of (request id, query_len,
+    seq_len) rows, and returns that step's metadata; with draw=True it also
+    draws q, k_new and v_new for the step's tokens from the stream's
+    generator (fp32 N(0,1) rounded to bf16, q first, then K, then V), so the
+    draws depend on the sequence of batches and on nothing else.
+    `initial_caches()` returns the pool's caches with every slot holding the
+    sentinels.
+    """
+
+    def __init__(self, seed: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 page_size: int, requests: Sequence[tuple], extra_pages: int = 0):
+        self.num_q_heads, self.num_kv_heads = int(num_q_heads), int(num_kv_heads)
+        self.head_dim, self.page_size = int(head_dim), int(page_size)
+        self.requests = [(int(p), int(m), int(a)) for p, m, a in requests]
+        P = self.page_size
+        counts = [(p + m + P - 1) // P for p, m, _ in self.requests]
+        self.num_blocks = sum(counts) + int(extra_pages)
+        self.max_blocks_per_seq = max([1] + counts)
+        self.rng = np.random.default_rng(seed)
+        perm = self.rng.permutation(self.num_blocks).astype(np.int32)
+        self.pages, off = [], 0
+        for n in counts:
+            self.pages.append(perm[off:off + n])
+            off += n
+
+    def initial_caches(self):
+        shape = (self.num_blocks, self.num_kv_heads, self.page_size, self.head_dim)
+        return (np.full(shape, SENTINEL_K, dtype=np.uint16),
+                np.full(shape, SENTINEL_V, dtype=np.uint16))
+
+    def step(self, batch, draw: bool = True) -> StepInputs:
+        P = self.page_size
+        S = len(batch)
+        ql = np.array([q for _, q, _ in batch], dtype=np.int32).reshape(S)
+        sl = np.array([n for _, _, n in batch], dtype=np.int32).reshape(S)
+        bt = np.full((max(S, 1), self.max_blocks_per_seq), -1, dtype=np.int32)[:S]
+        slots = []
+        for s, (rid, q, n) in enumerate(batch):
+            pg = self.pages[rid]
+            if (n + P - 1) // P > len(pg):
+                raise ValueError(f"request {rid}: seq_len {n} exceeds its pages")
+            bt[s, :len(pg)] = pg
+            pos = np.arange(n - q, n)
+            slots.append(pg[pos // P] * P + pos % P)
+        sm = (np.concatenate(slots) if slots else np.zeros(0, np.int64)).astype(np.int32)
+        T = int(ql.sum())
+        q = k = v = None
+        if draw:
+            q = normal_bf16(self.rng, (T, self.num_q_heads, self.head_dim))
+            k = normal_bf16(self.rng, (T, self.num_kv_heads, self.head_dim))
+            v = normal_bf16(self.rng, (T, self.num_kv_heads, self.head_dim))
+        return StepInputs(ql, sl, bt, sm, q, k, v)
+
+
+def llama3_8b_request_stream(seed: int = 41, num_requests: int = 16):
+    """A request stream for the step loop at the Llama-3-8B layer: prompts
+    uniform in [2048, 16384] tokens (the history range of the dynamic-chunking
+    design's sweep and beyond), 16..128 generated tokens, arrivals uniform over
+    the first 32 steps. Returns (prompt_len, max_new, arrival_step) triples."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(2048, 16385)), int(rng.integers(16, 129)),
+             int(rng.integers(0, 33))) for _ in range(num_requests)]

@@ -162,7 +162,8 @@ cpa_status cpa_plan_get_info(cpa_plan plan, cpa_plan_info* info);
  * workspace_bytes as returned by cpa_plan_create, 256-byte aligned), queued
  * on `stream`. A workspace holds one plan at a time: uploading another plan
  * into the same workspace replaces it, and cpa_attention then refuses the
- * first plan with CPA_ERR_WORKSPACE.
+ * first plan with CPA_ERR_WORKSPACE. The copy reads the plan's host-side
+ * image: keep the plan alive until `stream` has passed the upload.
  */
 cpa_status cpa_plan_upload(cpa_plan plan, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
