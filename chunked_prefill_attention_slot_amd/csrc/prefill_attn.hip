@@ -25,10 +25,11 @@
 //     sit in the B-operand layout of the second product;
 //   * the causal mask is applied only on tiles that cross the diagonal or
 //     the end of the key range (select -inf);
-//   * online softmax in fp32 with exp2 (scale*log2(e) folded into one FMA);
-//     the running max is only raised when a tile exceeds it by more than
-//     2^8, so the rescale of O is rare (weights stay below 256, exact in
-//     the final normalisation);
+//   * online softmax in fp32 with exp2 against a per-row bf16 reference
+//     (scale*log2(e) folded into Q, the reference subtracted inside the
+//     score product): the reference is set from the row max at the row's
+//     first visible key and moved only when a tile's weights sum past
+//     2^64, so a common tile forms no row max and O is rarely rescaled;
 //   * O^T += V^T.P^T on the same MFMA; the V^T operand comes from the [key][d]
 //     tile with ds_read_b64_tr_b16, which hands each lane four consecutive
 //     keys of one d column.
@@ -66,7 +67,7 @@ struct Cfg {
   static_assert(NKB == 2, "the row max tree assumes two 32-key blocks");
   static constexpr int NKS = D / 16;           // 16-wide d steps of K.Q^T
   static constexpr int NDB = D / 32;           // 32-row d blocks of V^T.P^T
-  static constexpr int NBUF = 3;               // LDS tile buffers
+  static constexpr int NBUF = 4;               // LDS tile buffers
   static constexpr int V_REGION = NBUF * TILE; // V tiles follow the K tiles
   static_assert(IPW >= 1, "tile too small for the wave count");
 };
@@ -306,35 +307,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  f32x16 sc[NKB];  // scores - m_ref (log2 units) of the current tile, S -> P phase
-
-  // S phase: S^T = K.Q^T for the tile in buffer B; the two 32-key blocks
-  // are accumulated alternately (two independent chains), K reads run four
-  // products ahead.
-  auto s_phase = [&](auto bc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
-    f32x16 acc[NKB];
-    const f32x16 zero = {};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc[kb] = mfma32(ones, qoff, zero);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 av =
-            *reinterpret_cast<const bf16x8*>(smem + (B * TILE + 32 * kb * ROWB) + kofs[ks]);
-        acc[kb] = mfma32(av, qf[ks], acc[kb]);
-      }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sc[kb] = acc[kb];
-    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);    // DS read
-    __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);  // offset products
-#pragma unroll
-    for (int i = 0; i < NKB * NKS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
-      if (i + 4 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
-    }
-  };
+  f32x16 sc[NKB];     // scores - m_ref (log2 units) of the newest tile
+  bf16x8 pw[2 * NKB]; // its bf16 weights, held for the next X phase
 
   // Causal mask offset by H, and the end of the key range. Accumulator i
   // of lane half hh holds key j0 + 32kb + 16(i>>3) + 8hh + (i&7).
@@ -403,21 +377,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     return __builtin_bit_cast(bf16x8, av);
   };
 
-  // P phase for tile t in buffer B: mask, row max, (rare) reference move,
-  // then the bf16 weights 2^(score - m_ref) of each 16-key half block, each followed by its four
-  // products O^T += V^T.P^T. The row sum adds the same bf16-rounded weights
-  // the product multiplies, so each output row is a convex combination of
-  // V. Pairs go to fdot2 as bf16x2 values (bit-casting elements of a u32x4
+  // bf16 weights 2^(score - m_ref) of the tile in the B-operand layout of the
+  // second product (half block 2kb+h2 of lane half hh: eight consecutive
+  // keys), and their sum. The sum adds the same bf16-rounded weights the
+  // product multiplies, so each output row is a convex combination of V.
+  // Pairs go to fdot2 as bf16x2 values (bit-casting elements of a u32x4
   // into it was miscompiled into four reads of the first element).
-  auto p_phase = [&](auto bc, int t) __attribute__((always_inline)) {
-    constexpr int B = decltype(bc)::value;
-    // The first half block's V operands do not wait for the softmax.
-    bf16x8 vpre[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vpre[db] = v_read(vofs[db] + B * TILE);
-    mask(it.kv0 + t * BN);
-    raise_ref(row_max());
+  auto weights = [&](bf16x8 (&pw)[2 * NKB]) __attribute__((always_inline)) -> float {
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float lt0 = 0.f, lt1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -428,101 +396,188 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j]);
           const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j + 1]);
           pp[j] = bf16x2{(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, l_run, false);
+          if (j & 1) lt1 = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, lt1, false);
+          else lt0 = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, lt0, false);
         }
-        const u32x4 pw = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+        const u32x4 w4 = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                           __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 av = (kb == 0 && h2 == 0)
-                                ? vpre[db]
-                                : v_read(vofs[db] + B * TILE + (32 * kb + 16 * h2) * ROWB);
-          oacc[db] = mfma32(av, pb, oacc[db]);
-        }
+        pw[2 * kb + h2] = __builtin_bit_cast(bf16x8, w4);
       }
-    // Weights of the first half block, then per product: the next weights
-    // on the VALU and V reads two products ahead.
-    __builtin_amdgcn_sched_group_barrier(0x0002, 24, 1);  // VALU
+    return lt0 + lt1;
+  };
+
+  // X phase: O^T += V^T.P^T for the previous tile (weights pw, V at LDS
+  // byte offset vbase) and S^T = K.Q^T for the current tile (K in buffer
+  // KB), all on the matrix core. Every score chain starts with the offset
+  // product; the two score chains and the four O chains are independent, so
+  // products issue back to back with the LDS reads running ahead of them.
+  // The first phase of an item has no previous tile (S only) and the last
+  // no current tile (PV only).
+  auto x_phase = [&](int vbase, auto kbc, auto pvc, auto sc_) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value;
+    constexpr bool PV = decltype(pvc)::value, S = decltype(sc_)::value;
+    f32x16 acc[NKB];
+    if constexpr (S) {
+      const f32x16 zero = {};
 #pragma unroll
-    for (int i = 0; i < NKB * 2 * NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x0002, 6, 1);  // VALU
-      if (i + 2 < NKB * 2 * NDB - NDB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
+      for (int kb = 0; kb < NKB; ++kb) acc[kb] = mfma32(ones, qoff, zero);
+    }
+#pragma unroll
+    for (int i = 0; i < NKB * NKS; ++i) {
+      if constexpr (PV) {
+        const int hb = i / NDB, db = i % NDB;
+        const bf16x8 av = v_read(vofs[db] + vbase + 16 * hb * ROWB);
+        oacc[db] = mfma32(av, pw[hb], oacc[db]);
+      }
+      if constexpr (S) {
+        const int kb = i % NKB, ks = i / NKB;
+        const bf16x8 av =
+            *reinterpret_cast<const bf16x8*>(smem + (KB * TILE + 32 * kb * ROWB) + kofs[ks]);
+        acc[kb] = mfma32(av, qf[ks], acc[kb]);
+      }
+    }
+    if constexpr (S) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = acc[kb];
+    }
+    if constexpr (PV && S) {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 6, 0);    // DS read
+      __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);  // offset products
+#pragma unroll
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);  // one PV, one S product
+        if (i + 2 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);
+      }
+    } else if constexpr (S) {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);
+#pragma unroll
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+        if (i + 4 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+        if (i + 2 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+      }
     }
   };
 
-  // Two wave groups in ping-pong. Group 0 (waves 0..NW/2-1) runs the phases
-  // S(0), P(0), S(1), P(1), ... one per half step; group 1 runs the same
-  // sequence one half step later, so on every SIMD one wave's score
-  // products overlap the other wave's softmax and V products. Tile t lives
-  // in LDS buffer t % 3; K(t) is read in half steps 2t, 2t+1 and V(t) in
-  // 2t+1, 2t+2, so the copy of tile t+3 into the same buffer is issued at
-  // the end of half step 2t+3 and awaited before half step 2t+6.
+  // Y phase for tile t: mask, then the weights against the current
+  // reference. The row max is only formed when a row has no reference yet
+  // or when the tile's weights sum past 2^64 (a score more than ~58 above
+  // the reference, or NaN from overflow): then the reference moves and the
+  // weights are formed again. Otherwise every weight is below 2^64 and its
+  // bf16 rounding and fp32 accumulation are as accurate as at any other
+  // scale (the two formats share fp32's exponent range), so no max is
+  // needed.
+  auto y_phase = [&](int t) __attribute__((always_inline)) {
+    mask(it.kv0 + t * BN);
+    float lt = weights(pw);
+    if (__builtin_amdgcn_ballot_w64(unset || !(lt <= 0x1p64f))) {
+      raise_ref(row_max());
+      lt = weights(pw);
+    }
+    l_run += lt;
+  };
+
+
+  // Two wave groups in ping-pong, half a tile apart. Group 0 (waves
+  // 0..NW/2-1) runs X(0) Y(0) X(1) Y(1) ... Y(n-1) X(n), one phase per half
+  // step, where X(s) is the products PV(s-1) + S(s) and Y(s) the weights of
+  // tile s; group 1 runs the same one half step later. On every SIMD one
+  // wave's products thus overlap the other wave's vector work. Tile s lives
+  // in LDS buffer s % 4: K(s) is read in half steps 2s, 2s+1 and V(s) in
+  // 2s+2, 2s+3, so tile s+4 may be copied into that buffer from half step
+  // 2s+4 on. Each wave issues its share of a tile's copy inside a Y phase
+  // (group 0 copies tile s+2 in Y(s), at half step 2s+1; group 1 copies
+  // tile s+3 in Y(s), at half step 2s+2), where the vector work leaves slack
+  // for the copy issue to stall; the copy of tile s is awaited before half
+  // step 2s.
   const int grp = w / (NW / 2);
   const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
+  // Wait until this wave's copy of tile s has landed, leaving the copies of
+  // later tiles (at most s+1, or 3 after the prologue) in flight.
+  auto wait_tile = [&](int s) __attribute__((always_inline)) {
+    const int ahead = min(ntiles - 1, max(3, s + 1)) - s;
+    if (ahead >= 3) {
+      if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    } else if (ahead == 2) {
+      if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else if (ahead == 1) {
+      if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
   if (ntiles > 0) {
-    issue(it.kv0, page_of(it.kv0), 0);
-    if (ntiles > 1) issue(it.kv0 + BN, page_of(it.kv0 + BN), 1);
-    if (ntiles > 2) issue(it.kv0 + 2 * BN, page_of(it.kv0 + 2 * BN), 2);
-    const int last = 2 * ntiles;  // half steps 0 .. last
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < ntiles) issue(it.kv0 + t * BN, page_of(it.kv0 + t * BN), t);
+    const int hend = 2 * ntiles;  // the steady half steps are 2 .. hend-1
     // Each group runs its own copy of the loop (same barriers, different
     // phase order), which keeps the register allocation of the two phase
     // sequences apart.
     auto run = [&](auto gc) __attribute__((always_inline)) {
       constexpr int G = decltype(gc)::value;
+      // Half steps 0 and 1: group 0 runs X(0) (scores only) then Y(0);
+      // group 1 idles, then runs X(0).
+      wait_tile(0);
+      __syncthreads();
+      if constexpr (G == 0) x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      __syncthreads();
+      if constexpr (G == 0) y_phase(0);
+      else x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      // Steady half steps h = 2 .. 2n-1: X(s) with 1 <= s <= n-1, Y(s) with
+      // s <= n-1 for either group, buffers known at compile time from h % 8.
       auto half = [&](auto jc, int h) __attribute__((always_inline)) {
-        constexpr int J = decltype(jc)::value;  // h % 6
-        if constexpr (J % 2 == 0) {
-          // Tile s = h/2 must have landed; copies of later tiles stay in flight.
-          const int s = h >> 1;
-          const int newest = (s + 1 >= 3) ? min(ntiles - 1, s + 1) : min(ntiles, 3) - 1;
-          const int ahead = newest - s;
-          if (ahead >= 2) {
-            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-          } else if (ahead == 1) {
-            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-          } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          }
-        }
+        constexpr int J = decltype(jc)::value;  // h % 8
+        if constexpr (J % 2 == 0) wait_tile(h >> 1);
         __syncthreads();
-        const int tn = (h + 3) >> 1;  // tile copied at the end of an odd half step
-        const bool copy = (J % 2 == 1) && h >= 3 && tn < ntiles;
-        int pg = -1;
-        if (copy) pg = page_of(it.kv0 + tn * BN);
-        if constexpr (G == 0) {
-          // phase h: S(h/2) or P((h-1)/2)
-          if constexpr (J % 2 == 0) {
-            if ((h >> 1) < ntiles) s_phase(ic<J / 2>{});
-          } else {
-            p_phase(ic<J / 2>{}, h >> 1);
-          }
+        constexpr bool X = ((J - G) & 1) == 0;       // X(s) when h - G is even
+        constexpr int SJ = ((J - G + 8) % 8) >> 1;  // s % 4
+        const int s = (h - G) >> 1;
+        if constexpr (X) {
+          x_phase(((SJ + 3) % 4) * TILE, ic<SJ>{}, std::true_type{}, std::true_type{});
         } else {
-          // phase h-1: P((h-2)/2) or S((h-1)/2)
-          if constexpr (J % 2 == 0) {
-            if (h >= 1) p_phase(ic<(J / 2 + 2) % 3>{}, (h - 1) >> 1);
-          } else {
-            s_phase(ic<J / 2>{});
-          }
+          constexpr int AH = 2 + G;                  // tile copied in this Y phase
+          const int tc = s + AH;
+          if (s + AH >= 4 && tc < ntiles)
+            issue(it.kv0 + tc * BN, page_of(it.kv0 + tc * BN), (SJ + AH) % 4);
+          y_phase(s);
         }
-        if (copy) issue(it.kv0 + tn * BN, pg, ((J + 3) / 2) % 3);
       };
-      for (int h0 = 0; h0 <= last; h0 += 6) {
-        half(ic<0>{}, h0);
-        if (h0 + 1 > last) break;
-        half(ic<1>{}, h0 + 1);
-        if (h0 + 2 > last) break;
-        half(ic<2>{}, h0 + 2);
-        if (h0 + 3 > last) break;
-        half(ic<3>{}, h0 + 3);
-        if (h0 + 4 > last) break;
-        half(ic<4>{}, h0 + 4);
-        if (h0 + 5 > last) break;
-        half(ic<5>{}, h0 + 5);
+      for (int h0 = 2; h0 < hend; h0 += 8) {
+        half(ic<2>{}, h0);
+        if (h0 + 1 >= hend) break;
+        half(ic<3>{}, h0 + 1);
+        if (h0 + 2 >= hend) break;
+        half(ic<4>{}, h0 + 2);
+        if (h0 + 3 >= hend) break;
+        half(ic<5>{}, h0 + 3);
+        if (h0 + 4 >= hend) break;
+        half(ic<6>{}, h0 + 4);
+        if (h0 + 5 >= hend) break;
+        half(ic<7>{}, h0 + 5);
+        if (h0 + 6 >= hend) break;
+        half(ic<0>{}, h0 + 6);
+        if (h0 + 7 >= hend) break;
+        half(ic<1>{}, h0 + 7);
       }
+      // Half steps 2n and 2n+1: group 0 runs X(n) (O only, V of tile n-1)
+      // then idles; group 1 runs Y(n-1) then X(n).
+      const int vlast = ((ntiles - 1) & 3) * TILE;
+      __syncthreads();
+      if constexpr (G == 0) x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
+      else y_phase(ntiles - 1);
+      __syncthreads();
+      if constexpr (G == 1) x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
     };
     if (grp == 0)
       run(ic<0>{});
