@@ -219,10 +219,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int lrow = lane / CPR, lpc = lane % CPR;
   const uint32_t smem_lds =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto page_of = [&](int j0) __attribute__((always_inline)) -> int {
+  // Block-table entry of this wave's rows of the tile at key j0, read from
+  // the staged copy; -1 past the key range. page_of makes it uniform. In the
+  // tile loop the entry is read one copy ahead, so the read's latency (it
+  // queues behind the other waves' operand reads) is not waited for.
+  auto page_raw = [&](int j0) __attribute__((always_inline)) -> int {
     const int key_w = j0 + w * IPW * RPI;
-    return __builtin_amdgcn_readfirstlane((key_w < j_end) ? s_pages[(key_w >> plog) - page0]
-                                                          : -1);
+    return (key_w < j_end) ? s_pages[(key_w >> plog) - page0] : -1;
+  };
+  auto page_of = [&](int j0) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_readfirstlane(page_raw(j0));
   };
   // Byte offsets of this lane's 16 bytes from the wave's first row (row
   // u*RPI + lrow of the wave's IPW*RPI, chunk swizzled to where it lands).
@@ -316,12 +322,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     if ((j0 + BN - 1 > it.hist + it.q0) || (j0 + BN > it.kv1)) {
       // key = j0 + 8hh + c with c a compile-time constant per accumulator;
       // the key is visible iff c < lim.
-      const int lim = min(qpos + 1, it.kv1) - j0 - 8 * hh;
+      // Bit select against an arithmetic-shift mask rather than a compare
+      // per score: 32 compares would each hold a lane mask in scalar
+      // registers.
+      const int lim1 = min(qpos + 1, it.kv1) - j0 - 8 * hh - 1;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kb + 16 * (i >> 3) + (i & 7) >= lim) sc[kb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t m = (uint32_t)((lim1 - (32 * kb + 16 * (i >> 3) + (i & 7))) >> 31);
+          uint32_t v;
+          asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(v) : "v"(m), "v"(0xFF800000u),
+              "v"(__float_as_uint(sc[kb][i])));
+          sc[kb][i] = __uint_as_float(v);
+        }
     }
   };
   // Row max over both lane halves (same query).
@@ -379,13 +393,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 
   // bf16 weights 2^(score - m_ref) of the tile in the B-operand layout of the
   // second product (half block 2kb+h2 of lane half hh: eight consecutive
-  // keys), and their sum. The sum adds the same bf16-rounded weights the
-  // product multiplies, so each output row is a convex combination of V.
-  // Pairs go to fdot2 as bf16x2 values (bit-casting elements of a u32x4
-  // into it was miscompiled into four reads of the first element).
+  // keys), and the sum of the fp32 weights before rounding, in four add
+  // chains. The sum uses plain fp32 adds: a dot-product instruction (bf16
+  // pairs dotted with ones) does not issue beside the other wave's matrix
+  // products and serialised the two wave groups. Summing the unrounded
+  // weights is as accurate as summing the rounded ones; constant V then
+  // comes back within the bf16 rounding of the weights (relative 2^-8)
+  // instead of exactly.
   auto weights = [&](bf16x8 (&pw)[2 * NKB]) __attribute__((always_inline)) -> float {
-    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float lt0 = 0.f, lt1 = 0.f;
+    float lt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -396,14 +412,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           const float p0 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j]);
           const float p1 = __builtin_amdgcn_exp2f(sc[kb][8 * h2 + 2 * j + 1]);
           pp[j] = bf16x2{(__bf16)p0, (__bf16)p1};
-          if (j & 1) lt1 = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, lt1, false);
-          else lt0 = __builtin_amdgcn_fdot2_f32_bf16(pp[j], one2, lt0, false);
+          lt[j] += p0 + p1;
         }
         const u32x4 w4 = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                           __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
         pw[2 * kb + h2] = __builtin_bit_cast(bf16x8, w4);
       }
-    return lt0 + lt1;
+    return (lt[0] + lt[1]) + (lt[2] + lt[3]);
   };
 
   // X phase: O^T += V^T.P^T for the previous tile (weights pw, V at LDS
@@ -526,6 +541,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     // sequences apart.
     auto run = [&](auto gc) __attribute__((always_inline)) {
       constexpr int G = decltype(gc)::value;
+      // Block-table entry (not yet uniform) for the copy of this wave's next
+      // Y phase: Y(s) copies tile s + 2 + G.
+      int pg_next = page_raw(it.kv0 + (2 + G + (G == 0 ? 1 : 0)) * BN);
       // Half steps 0 and 1: group 0 runs X(0) (scores only) then Y(0);
       // group 1 idles, then runs X(0).
       wait_tile(0);
@@ -549,7 +567,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           constexpr int AH = 2 + G;                  // tile copied in this Y phase
           const int tc = s + AH;
           if (s + AH >= 4 && tc < ntiles)
-            issue(it.kv0 + tc * BN, page_of(it.kv0 + tc * BN), (SJ + AH) % 4);
+            issue(it.kv0 + tc * BN, __builtin_amdgcn_readfirstlane(pg_next), (SJ + AH) % 4);
+          pg_next = page_raw(it.kv0 + (tc + 1) * BN);
           y_phase(s);
         }
       };
