@@ -337,7 +337,9 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   p->off_combine = off;
   off = cpa::round_up(off + p->combine.size() * sizeof(cpa::CombineItem), cpa::kAlign);
   p->off_part_o = off;
-  off = cpa::round_up(off + (size_t)p->part_rows * desc->head_dim * sizeof(float), cpa::kAlign);
+  // Split partials O/l are kept in the output's precision.
+  const size_t part_elem = desc->out_dtype == CPA_DTYPE_F32 ? sizeof(float) : sizeof(uint16_t);
+  off = cpa::round_up(off + (size_t)p->part_rows * desc->head_dim * part_elem, cpa::kAlign);
   p->off_part_ml = off;
   off = cpa::round_up(off + (size_t)p->part_rows * 2 * sizeof(float), cpa::kAlign);
   p->ws_bytes = std::max(off, cpa::kAlign);
@@ -440,7 +442,7 @@ cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache, cons
   a.scale_log2e = d.scale * 1.4426950408889634f;
   a.out = out;
   a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
-  a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  a.part_o = ws + plan->off_part_o;
   a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
   a.zeros = reinterpret_cast<const uint16_t*>(ws);
 

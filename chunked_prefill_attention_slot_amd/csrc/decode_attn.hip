@@ -205,9 +205,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = o2;
       }
     } else {
+      // Partial of a split key range: O/l in the output's precision.
       const size_t prow = (size_t)it.part + g;
-      f32x4 o4 = {oo[0], oo[1], oo[2], oo[3]};
-      *reinterpret_cast<f32x4*>(a.part_o + prow * D + d) = o4;
+      const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
+      if (a.out_f32) {
+        f32x4 o4 = {oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + prow * D + d) = o4;
+      } else {
+        u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + prow * D + d) = o2;
+      }
       if (d == 0) {
         a.part_ml[prow * 2 + 0] = mm;
         a.part_ml[prow * 2 + 1] = ll;
@@ -217,32 +224,63 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
 }
 
 // Log-sum-exp merge of the split partials of one tile: thread -> (packed
-// row r, 4 consecutive d).
-template <int D>
+// row r, 4 consecutive d). Split k holds O_k/l_k, max m_k and sum l_k;
+// O = sum_k 2^(m_k - m) l_k (O_k/l_k) / sum_k 2^(m_k - m) l_k, m = max_k m_k.
+template <int D, bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
                                                       AttnArgs a) {
   constexpr int D4 = D / 4;
+  constexpr int B = 8;  // splits read per batch
   const CombineItem it = items[blockIdx.x];
   const int idx = blockIdx.y * 256 + threadIdx.x;
   const int r = idx / D4, d = 4 * (idx % D4);
   if (r >= it.rows) return;
-  float mm = -INFINITY;
-  for (int k = 0; k < it.nsplit; ++k)
-    mm = fmaxf(mm, a.part_ml[((size_t)it.part0 + (size_t)k * it.rows + r) * 2]);
-  float ll = 0.f;
+  // Every load of a batch is issued before any is used (indices past the
+  // last split repeat it and get weight 0), so a batch of eight splits
+  // costs one round trip to memory; earlier batches are rescaled to the
+  // running max.
+  float mm = -INFINITY, ll = 0.f;
   f32x4 oo = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < it.nsplit; ++k) {
-    const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
-    const float mk = a.part_ml[prow * 2];
-    const float wk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - mm);
-    ll = fmaf(wk, a.part_ml[prow * 2 + 1], ll);
-    const f32x4 ok = *reinterpret_cast<const f32x4*>(a.part_o + prow * D + d);
-    oo += wk * ok;
+  for (int k0 = 0; k0 < it.nsplit; k0 += B) {
+    float mk[B], lk[B];
+    f32x4 ok[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int k = min(k0 + j, it.nsplit - 1);
+      const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
+      mk[j] = a.part_ml[prow * 2];
+      lk[j] = a.part_ml[prow * 2 + 1];
+      if constexpr (F32) {
+        ok[j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + prow * D + d);
+      } else {
+        const u32x2 b = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) +
+                                                         prow * D + d);
+        ok[j] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+      }
+    }
+    float bm = mm;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (k0 + j >= it.nsplit) mk[j] = -INFINITY;
+      bm = fmaxf(bm, mk[j]);
+    }
+    const float a0 = (mm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm - bm);
+    ll *= a0;
+    oo *= a0;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      // Weight of split k: its sum l_k scaled to the common max; the stored
+      // partial is O_k / l_k.
+      const float wk = (mk[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[j] - bm) * lk[j];
+      ll += wk;
+      oo += wk * ok[j];
+    }
+    mm = bm;
   }
   const float inv = 1.f / ll;
   const int qi = r / it.nheads, hl = r - qi * it.nheads;
   const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D + d;
-  if (a.out_f32) {
+  if constexpr (F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob) = oo * inv;
   } else {
     u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
@@ -278,10 +316,14 @@ hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows,
   if (num_items == 0) return hipSuccess;
   const int threads = max_rows * (head_dim / 4);
   const dim3 grid(num_items, (threads + 255) / 256);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, items, a);
+  if (head_dim == 128 && a.out_f32)
+    hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(256), 0, stream, items, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(256), 0, stream, items, a);
+  else if (head_dim == 64 && a.out_f32)
+    hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(256), 0, stream, items, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, items, a);
+    hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(256), 0, stream, items, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -630,15 +630,24 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         }
       }
   } else {
+    // Partial of a split key range: O/l in the output's precision (a row
+    // with no visible key in the range has l = 0 and stores zeros).
     const size_t prow = (size_t)it.part + r;
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * db + 8 * g4 + 4 * hh;
-        f32x4 o4 = {oacc[db][4 * g4 + 0], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
-                    oacc[db][4 * g4 + 3]};
-        *reinterpret_cast<f32x4*>(a.part_o + prow * D + d) = o4;
+        const float v0 = oacc[db][4 * g4 + 0] * inv, v1 = oacc[db][4 * g4 + 1] * inv;
+        const float v2 = oacc[db][4 * g4 + 2] * inv, v3 = oacc[db][4 * g4 + 3] * inv;
+        if (a.out_f32) {
+          f32x4 o4 = {v0, v1, v2, v3};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + prow * D + d) = o4;
+        } else {
+          u32x2 o2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + prow * D + d) = o2;
+        }
       }
     if (hh == 0) {
       a.part_ml[prow * 2 + 0] = unset ? -INFINITY : m_ref;
