@@ -25,11 +25,12 @@
 //     sit in the B-operand layout of the second product;
 //   * the causal mask is applied only on tiles that cross the diagonal or
 //     the end of the key range (select -inf);
-//   * online softmax in fp32 with exp2 against a per-row bf16 reference
-//     (scale*log2(e) folded into Q, the reference subtracted inside the
-//     score product): the reference is set from the row max at the row's
-//     first visible key and moved only when a tile's weights sum past
-//     2^64, so a common tile forms no row max and O is rarely rescaled;
+//   * online softmax in fp32 with exp2 against a per-row reference
+//     (scale*log2(e) folded into Q): the reference is 0 unless the row's
+//     scores leave [-64, 64] (then it is subtracted on the vector ALU), set
+//     at the row's first visible key and moved only when a tile's weights
+//     sum past 2^64, so a common tile forms no row max and O is rarely
+//     rescaled;
 //   * O^T += V^T.P^T on the same MFMA; the V^T operand comes from the [key][d]
 //     tile with ds_read_b64_tr_b16, which hands each lane four consecutive
 //     keys of one d column.
@@ -116,13 +117,6 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
-}
-
-// Smallest bf16 value >= x (x finite).
-__device__ __forceinline__ float bf16_ceil(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = (x > 0.f) ? ((u + 0xFFFFu) & 0xFFFF0000u) : (u & 0xFFFF0000u);
-  return __uint_as_float(u);
 }
 
 // 16-byte chunk swizzle of K row r. The eight lanes of one ds_read_b128
@@ -239,7 +233,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     koff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ k_swz<CPR>(row)) * 8) * 2);
     voff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ v_swz<CPR>(row)) * 8) * 2);
   }
-  auto issue = [&](int j0, int pg, int buf) __attribute__((always_inline)) {
+  // PARTS selects the matrices copied: 1 = K, 2 = V, 3 = both.
+  auto issue = [&](int j0, int pg, int buf, auto parts) __attribute__((always_inline)) {
+    constexpr int PARTS = decltype(parts)::value;
     const uint32_t kbuf = smem_lds + buf * TILE;
     const uint32_t vbuf = smem_lds + V_REGION + buf * TILE;
     const int key_w = j0 + w * IPW * RPI;
@@ -249,8 +245,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 #pragma unroll
       for (int u = 0; u < IPW; ++u) {
         const int i = w * IPW + u;
-        lds_dma16_s(a.k_cache + e0, koff[u], kbuf + i * 1024);
-        lds_dma16_s(a.v_cache + e0, voff[u], vbuf + i * 1024);
+        if constexpr (PARTS & 1) lds_dma16_s(a.k_cache + e0, koff[u], kbuf + i * 1024);
+        if constexpr (PARTS & 2) lds_dma16_s(a.v_cache + e0, voff[u], vbuf + i * 1024);
       }
       return;
     }
@@ -269,10 +265,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
         vs = a.v_cache + base + (lpc ^ v_swz<CPR>(row)) * 8;
       }
-      lds_dma16(ks, __builtin_amdgcn_readfirstlane(kbuf + i * 1024));
-      lds_dma16(vs, __builtin_amdgcn_readfirstlane(vbuf + i * 1024));
+      if constexpr (PARTS & 1) lds_dma16(ks, __builtin_amdgcn_readfirstlane(kbuf + i * 1024));
+      if constexpr (PARTS & 2) lds_dma16(vs, __builtin_amdgcn_readfirstlane(vbuf + i * 1024));
     }
   };
+
 
   // Per-lane LDS offsets of the operand reads; the tile buffer and the
   // 32-key block add compile-time constants.
@@ -296,24 +293,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
                (((4 * db + (vd_off >> 3)) ^ v_swz<CPR>(vkey_off)) << 4) + ((vd_off & 7) << 1);
   const auto* smem3 = (const __attribute__((address_space(3))) uint8_t*)smem;
 
-  // Reference offset of this row in log2 units: a bf16 value that no score
-  // seen so far exceeds by more than 8 (scores are taken relative to it
-  // inside the score product); unset before the row's first visible key.
+  // Reference of this row in log2 units: the weights are 2^(score - m_ref).
+  // It is 0 unless the row's scores leave [-64, 64] (then the weights would
+  // leave the range in which their sums are safe), so for common inputs no
+  // subtraction is needed at all; unset before the row's first visible key.
   float m_ref = 0.f;
   bool unset = true;
   float l_run = 0.f;         // this lane's part of the row sum
-  // Offset product ONES x QOFF adds -m_ref to every score of the column:
-  // the B operand holds -m_ref at k = 0 (lanes of half 0), zeros elsewhere.
-  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-  bf16x8 qoff = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f,
-                 (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  f32x16 sc[NKB];     // scores - m_ref (log2 units) of the newest tile
+  f32x16 sc[NKB];     // scores (log2 units) of the newest tile
   bf16x8 pw[2 * NKB]; // its bf16 weights, held for the next X phase
 
   // Causal mask offset by H, and the end of the key range. Accumulator i
@@ -352,21 +344,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
                                                      false, false);
     return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
   };
-  // Move the reference only when a score would exceed it by more than 8
-  // (weights above 2^8; rare: O and l are rescaled and this tile's scores
-  // shifted), or to the first visible score of the row. The new reference is
-  // rounded up to bf16 so that the offset product represents it exactly.
+  // Set the reference at the row's first visible key (0 when the row max
+  // mx, relative to the current reference, lies in [-64, 64], else mx), and
+  // move it to the row max when a score exceeds it by more than 32 (rare:
+  // O and l are rescaled and this tile's scores shifted). sc holds the
+  // scores relative to the current reference.
   auto raise_ref = [&](float mx) __attribute__((always_inline)) {
-    const bool need = unset ? (mx > -INFINITY) : (mx > 8.f);
+    const bool need = unset ? (mx > -INFINITY) : (mx > 32.f);
     if (__builtin_amdgcn_ballot_w64(need)) {
       float alpha = 1.f, delta = 0.f;
       if (need) {
-        const float m_new = bf16_ceil(m_ref + mx);
+        const float m_new = (unset && fabsf(mx) <= 64.f) ? m_ref : m_ref + mx;
         alpha = unset ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         delta = m_ref - m_new;
         m_ref = m_new;
         unset = false;
-        if (hh == 0) qoff[0] = (__bf16)(-m_ref);
       }
       l_run *= alpha;
 #pragma unroll
@@ -423,9 +415,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 
   // X phase: O^T += V^T.P^T for the previous tile (weights pw, V at LDS
   // byte offset vbase) and S^T = K.Q^T for the current tile (K in buffer
-  // KB), all on the matrix core. Every score chain starts with the offset
-  // product; the two score chains and the four O chains are independent, so
-  // products issue back to back with the LDS reads running ahead of them.
+  // KB), all on the matrix core. The two score chains and the four O chains
+  // are independent, so products issue back to back with the LDS reads
+  // running ahead of them.
   // The first phase of an item has no previous tile (S only) and the last
   // no current tile (PV only).
   auto x_phase = [&](int vbase, auto kbc, auto pvc, auto sc_) __attribute__((always_inline)) {
@@ -433,9 +425,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     constexpr bool PV = decltype(pvc)::value, S = decltype(sc_)::value;
     f32x16 acc[NKB];
     if constexpr (S) {
-      const f32x16 zero = {};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) acc[kb] = mfma32(ones, qoff, zero);
+      for (int kb = 0; kb < NKB; ++kb) acc[kb] = f32x16{};
     }
 #pragma unroll
     for (int i = 0; i < NKB * NKS; ++i) {
@@ -457,7 +448,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     }
     if constexpr (PV && S) {
       __builtin_amdgcn_sched_group_barrier(0x0100, 6, 0);    // DS read
-      __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);  // offset products
 #pragma unroll
       for (int i = 0; i < NKB * NKS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);  // one PV, one S product
@@ -465,7 +455,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       }
     } else if constexpr (S) {
       __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, NKB, 0);
 #pragma unroll
       for (int i = 0; i < NKB * NKS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
@@ -491,6 +480,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   // needed.
   auto y_phase = [&](int t) __attribute__((always_inline)) {
     mask(it.kv0 + t * BN);
+    if (__builtin_amdgcn_ballot_w64(m_ref != 0.f)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] -= m_ref;
+    }
     float lt = weights(pw);
     if (__builtin_amdgcn_ballot_w64(unset || !(lt <= 0x1p64f))) {
       raise_ref(row_max());
@@ -501,17 +496,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 
 
   // Two wave groups in ping-pong, half a tile apart. Group 0 (waves
-  // 0..NW/2-1) runs X(0) Y(0) X(1) Y(1) ... Y(n-1) X(n), one phase per half
-  // step, where X(s) is the products PV(s-1) + S(s) and Y(s) the weights of
-  // tile s; group 1 runs the same one half step later. On every SIMD one
-  // wave's products thus overlap the other wave's vector work. Tile s lives
-  // in LDS buffer s % 4: K(s) is read in half steps 2s, 2s+1 and V(s) in
-  // 2s+2, 2s+3, so tile s+4 may be copied into that buffer from half step
-  // 2s+4 on. Each wave issues its share of a tile's copy inside a Y phase
-  // (group 0 copies tile s+2 in Y(s), at half step 2s+1; group 1 copies
-  // tile s+3 in Y(s), at half step 2s+2), where the vector work leaves slack
-  // for the copy issue to stall; the copy of tile s is awaited before half
-  // step 2s.
+  // 0..NW/2-1) runs X(0) Y(0) X(1) Y(1) ... Y(n-1) X(n), where X(s) is the
+  // products PV(s-1) + S(s) and Y(s) the weights of tile s; group 1 runs the
+  // same half a tile later. On every SIMD one wave's products thus overlap
+  // the other wave's vector work. Tile s lives in LDS buffer s % 4. One
+  // barrier per tile, at the start of tile interval s (half steps 2s and
+  // 2s+1, in which group 0 runs X(s) Y(s) and group 1 runs Y(s-1) X(s)),
+  // after each wave has waited for its copies of tile s: it publishes K(s)
+  // for both groups' X(s), and V(s-1) was published one interval earlier.
+  // Each wave issues its share of a tile's copy inside a Y phase (group 0
+  // copies tile s+2 in Y(s), group 1 copies tile s+2 in Y(s-1)), both in
+  // interval s, into the buffer of tile s-2, whose last readers, X(s-2) and
+  // X(s-1), finished in earlier intervals. The vector work leaves slack for
+  // the copy issue to stall.
   const int grp = w / (NW / 2);
   const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
   // Wait until this wave's copy of tile s has landed, leaving the copies of
@@ -534,7 +531,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   if (ntiles > 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      if (t < ntiles) issue(it.kv0 + t * BN, page_of(it.kv0 + t * BN), t);
+      if (t < ntiles) issue(it.kv0 + t * BN, page_of(it.kv0 + t * BN), t, ic<3>{});
     const int hend = 2 * ntiles;  // the steady half steps are 2 .. hend-1
     // Each group runs its own copy of the loop (same barriers, different
     // phase order), which keeps the register allocation of the two phase
@@ -545,19 +542,23 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       // Y phase: Y(s) copies tile s + 2 + G.
       int pg_next = page_raw(it.kv0 + (2 + G + (G == 0 ? 1 : 0)) * BN);
       // Half steps 0 and 1: group 0 runs X(0) (scores only) then Y(0);
-      // group 1 idles, then runs X(0).
+      // group 1 runs X(0).
       wait_tile(0);
       __syncthreads();
-      if constexpr (G == 0) x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
-      __syncthreads();
-      if constexpr (G == 0) y_phase(0);
-      else x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      if constexpr (G == 0) {
+        x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+        y_phase(0);
+      } else {
+        x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      }
       // Steady half steps h = 2 .. 2n-1: X(s) with 1 <= s <= n-1, Y(s) with
       // s <= n-1 for either group, buffers known at compile time from h % 8.
       auto half = [&](auto jc, int h) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;  // h % 8
-        if constexpr (J % 2 == 0) wait_tile(h >> 1);
-        __syncthreads();
+        if constexpr (J % 2 == 0) {
+          wait_tile(h >> 1);
+          __syncthreads();
+        }
         constexpr bool X = ((J - G) & 1) == 0;       // X(s) when h - G is even
         constexpr int SJ = ((J - G + 8) % 8) >> 1;  // s % 4
         const int s = (h - G) >> 1;
@@ -566,10 +567,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         } else {
           constexpr int AH = 2 + G;                  // tile copied in this Y phase
           const int tc = s + AH;
-          if (s + AH >= 4 && tc < ntiles)
-            issue(it.kv0 + tc * BN, __builtin_amdgcn_readfirstlane(pg_next), (SJ + AH) % 4);
+          // The copy is issued after the vector work: the issue stalls
+          // while the address unit drains the other waves' copies, and the
+          // stall then overlaps the wait at the barrier.
+          const bool copy = s + AH >= 4 && tc < ntiles;
+          const int pg = __builtin_amdgcn_readfirstlane(pg_next);
           pg_next = page_raw(it.kv0 + (tc + 1) * BN);
           y_phase(s);
+          if (copy) issue(it.kv0 + tc * BN, pg, (SJ + AH) % 4, ic<3>{});
         }
       };
       for (int h0 = 2; h0 < hend; h0 += 8) {
@@ -589,14 +594,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         if (h0 + 7 >= hend) break;
         half(ic<1>{}, h0 + 7);
       }
-      // Half steps 2n and 2n+1: group 0 runs X(n) (O only, V of tile n-1)
-      // then idles; group 1 runs Y(n-1) then X(n).
+      // Half steps 2n and 2n+1: group 0 runs X(n) (O only, V of tile n-1);
+      // group 1 runs Y(n-1) then X(n).
       const int vlast = ((ntiles - 1) & 3) * TILE;
       __syncthreads();
-      if constexpr (G == 0) x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
-      else y_phase(ntiles - 1);
-      __syncthreads();
-      if constexpr (G == 1) x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
+      if constexpr (G == 1) y_phase(ntiles - 1);
+      x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
     };
     if (grp == 0)
       run(ic<0>{});

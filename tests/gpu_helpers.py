@@ -16,10 +16,10 @@ MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 
 
-def oracle_out(b, rows=None):
+def oracle_out(b, rows=None, scale=None):
     kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
     return paged_attention(b.q, kc, vc, b.block_table, b.query_lens, b.seq_lens,
-                           b.num_kv_heads, b.page_size, rows=rows)
+                           b.num_kv_heads, b.page_size, scale=scale, rows=rows)
 
 
 def compare(got: np.ndarray, ref: np.ndarray, label: str = ""):

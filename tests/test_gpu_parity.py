@@ -88,6 +88,31 @@ def test_random_shapes(H, shape):
     run_and_compare(H, b, f"shape {shape}")
 
 
+@pytest.mark.parametrize("shift", [(0.0, 0.0), (2.5, 2.5), (2.5, -2.5)])
+def test_large_scores(H, shift):
+    """Q and K moved by offsets (a, b): every score gains ~d*a*b*scale
+    (about +-100 in log2 units at 2.5), which leaves the softmax nearly flat
+    but puts all scores far outside [-64, 64], so rows take a nonzero
+    reference at their first visible key; split and unsplit items alike."""
+    from chunked_prefill_attention_slot_amd.inputs import f32_to_bf16_bits
+    b = make(seed=12, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+             query_lens=[300, 70], seq_lens=[3000, 70], extra_pages=1)
+
+    def moved(bits, c):
+        x = (bits.astype(np.uint32) << 16).view(np.float32)
+        return f32_to_bf16_bits(x / 4 + c)
+
+    b.q = moved(b.q, shift[0])
+    b.k_new, b.k_cache = moved(b.k_new, shift[1]), moved(b.k_cache, shift[1])
+    label = f"large scores shift {shift}"
+    banner(label)
+    ref = H.oracle_out(b)
+    for opts in (None, {"prefill_split": 1}):
+        db = H.DeviceBatch(b, out_dtype=1, options=opts)
+        db.run()
+        H.compare(db.out_f64(), ref, f"{label} {opts}")
+
+
 def test_forced_splits_agree(H):
     b = make(seed=7, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
              query_lens=[256], seq_lens=[3000], extra_pages=1)
