@@ -513,15 +513,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int ntiles = (it.kv0 < j_end) ? (j_end - it.kv0 + BN - 1) / BN : 0;
   // Wait until this wave's copy of tile s has landed, leaving the copies of
   // later tiles (at most s+1, or 3 after the prologue) in flight.
+  // Every wave has issued its copies of tiles up to s+1 (when they exist)
+  // by the time it waits for tile s.
   auto wait_tile = [&](int s) __attribute__((always_inline)) {
-    const int ahead = min(ntiles - 1, max(3, s + 1)) - s;
-    if (ahead >= 3) {
-      if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    } else if (ahead == 2) {
-      if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else if (ahead == 1) {
+    const int ahead = min(ntiles - 1, s + 1) - s;
+    if (ahead == 1) {
       if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     } else {
@@ -529,8 +525,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     }
   };
   if (ntiles > 0) {
+    // Tiles 0 and 1 are copied before the loop; the loop copies tile s+2
+    // in tile interval s from then on (tile 2 after the X(0) of group 1 and
+    // in the Y(0) of group 0).
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
       if (t < ntiles) issue(it.kv0 + t * BN, page_of(it.kv0 + t * BN), t, ic<3>{});
     const int hend = 2 * ntiles;  // the steady half steps are 2 .. hend-1
     // Each group runs its own copy of the loop (same barriers, different
@@ -539,18 +538,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     auto run = [&](auto gc) __attribute__((always_inline)) {
       constexpr int G = decltype(gc)::value;
       // Block-table entry (not yet uniform) for the copy of this wave's next
-      // Y phase: Y(s) copies tile s + 2 + G.
-      int pg_next = page_raw(it.kv0 + (2 + G + (G == 0 ? 1 : 0)) * BN);
+      // Y phase in the loop: Y(s) copies tile s + 2 + G, the first one tile 3.
+      int pg_next = page_raw(it.kv0 + 3 * BN);
+      const int pg2 = page_of(it.kv0 + 2 * BN);
       // Half steps 0 and 1: group 0 runs X(0) (scores only) then Y(0);
-      // group 1 runs X(0).
+      // group 1 runs X(0). Both then copy their share of tile 2.
       wait_tile(0);
       __syncthreads();
-      if constexpr (G == 0) {
-        x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
-        y_phase(0);
-      } else {
-        x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
-      }
+      x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      if constexpr (G == 0) y_phase(0);
+      if (2 < ntiles) issue(it.kv0 + 2 * BN, pg2, 2, ic<3>{});
       // Steady half steps h = 2 .. 2n-1: X(s) with 1 <= s <= n-1, Y(s) with
       // s <= n-1 for either group, buffers known at compile time from h % 8.
       auto half = [&](auto jc, int h) __attribute__((always_inline)) {
@@ -570,7 +567,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           // The copy is issued after the vector work: the issue stalls
           // while the address unit drains the other waves' copies, and the
           // stall then overlaps the wait at the barrier.
-          const bool copy = s + AH >= 4 && tc < ntiles;
+          const bool copy = tc < ntiles;
           const int pg = __builtin_amdgcn_readfirstlane(pg_next);
           pg_next = page_raw(it.kv0 + (tc + 1) * BN);
           y_phase(s);
