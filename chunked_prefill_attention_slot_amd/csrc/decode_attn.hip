@@ -16,6 +16,8 @@
 //     combine_kernel (log-sum-exp weights).
 #include <math.h>
 
+#include <type_traits>
+
 #include "cpa_internal.h"
 
 namespace cpa {
@@ -32,6 +34,24 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Sum over aligned groups of N lanes (N = 4, 8 or 16), left in every lane of
+// the group, with DPP moves on the vector ALU: swap neighbours, swap pairs
+// (a quad then holds its sum in every lane), mirror each half row (the
+// other quad of the eight), mirror the row (the other eight of the 16).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                           decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+  if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+  return x;
 }
 
 // Merge (m2, l2, o2) into (m, l, o); m in log2 units, -inf = empty.
@@ -87,6 +107,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
   const int plog = a.page_log2, pmask = (1 << plog) - 1;
   const size_t head_off = (size_t)it.kvh << plog;
 
+  // Block-table entries of this lane's keys, read one iteration ahead of
+  // the K/V loads that use them, so an iteration costs one round trip to
+  // memory instead of two.
+  auto pages_of = [&](int base, int (&pg)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPB + w * KPW + ks;
+      pg[u] = (key < it.kv1) ? bt[key >> plog] : -1;
+    }
+  };
+  int pg_cur[U];
+  pages_of(it.kv0, pg_cur);
   for (int base = it.kv0; base < it.kv1; base += U * KPB) {
     u32x4 kr[U], vr[U];
     bool ok[U];
@@ -96,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
       ok[u] = key < it.kv1;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (ok[u]) {
-        const int page = bt[key >> plog];
+        const int page = pg_cur[u];
         if ((unsigned)page < (unsigned)a.num_blocks) {
           const size_t off =
               (((size_t)page * a.num_kv_heads << plog) + head_off + (key & pmask)) * D + 8 * c;
@@ -107,6 +139,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
       kr[u] = kv;
       vr[u] = vv;
     }
+    pages_of(base + U * KPB, pg_cur);
 
     float s[U][G];
 #pragma unroll
@@ -122,8 +155,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(qv[g][e], kf[e], acc);
-#pragma unroll
-        for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
+        acc = group_sum<LPK>(acc);
         s[u][g] = ok[u] ? acc * sl2e : -INFINITY;
       }
     }
