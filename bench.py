@@ -53,13 +53,62 @@ def flops_chunk(hq, d, c, h):
     return 4.0 * hq * d * c * (h + c / 2.0)
 
 
+_HIP = None
+
+
+class Event:
+    """A HIP timing event on torch's current stream, created with
+    hipEventDisableSystemFence. A default event record ends with a
+    system-scope fence: it writes back and invalidates the caches, which
+    costs time inside the bracket and slows the work after it. Timing-only
+    events do not need it (HIP's own documentation of the flag says so).
+    Same interface as torch.cuda.Event: record(), synchronize(),
+    elapsed_time(end) in ms."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch
+        global _HIP
+        if _HIP is None:
+            torch.cuda.init()
+            # The HIP runtime torch (and libcpa) already use in this process.
+            path = [l.split()[-1] for l in open("/proc/self/maps").read().splitlines()
+                    if "libamdhip64" in l][0]
+            _HIP = ctypes.CDLL(path)
+        self._ctypes = ctypes
+        # Recorded on the stream current at creation (the timed loops run there).
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.h = ctypes.c_void_p()
+        rc = _HIP.hipEventCreateWithFlags(ctypes.byref(self.h),
+                                          ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        assert rc == 0, f"hipEventCreateWithFlags: {rc}"
+
+    def record(self):
+        rc = _HIP.hipEventRecord(self.h, self._stream)
+        assert rc == 0, f"hipEventRecord: {rc}"
+
+    def synchronize(self):
+        rc = _HIP.hipEventSynchronize(self.h)
+        assert rc == 0, f"hipEventSynchronize: {rc}"
+
+    def elapsed_time(self, end):
+        ms = self._ctypes.c_float()
+        rc = _HIP.hipEventElapsedTime(self._ctypes.byref(ms), self.h, end.h)
+        assert rc == 0, f"hipEventElapsedTime: {rc}"
+        return ms.value
+
+    def __del__(self):
+        if _HIP is not None and self.h:
+            _HIP.hipEventDestroy(self.h)
+
+
 def median_ms(fn, reps, warmup):
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
+    ev = [(Event(), Event()) for _ in range(reps)]
     for s, e in ev:
         s.record()
         fn()
@@ -85,10 +134,14 @@ def headline(args):
     hq, d = 32, 128
     flops = [flops_chunk(hq, d, CHUNK, h) for h in args.hist]
 
+    # Each call's arguments are marshalled once (binding.bind_*): the timed
+    # loop then costs one foreign call per launch on the host.
+    calls = [db.bound() for _, db in dbs]
+
     def step():
-        for _, db in dbs:
-            db.kv_write()
-            db.attention()
+        for kv_write, attention in calls:
+            kv_write()
+            attention()
 
     for _ in range(args.warmup):
         step()
@@ -96,19 +149,19 @@ def headline(args):
     # Per-call events on the launch stream (torch's current stream), inside
     # the timed region.
     n = len(dbs)
-    ev_attn = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_attn = [[(Event(), Event())
                 for _ in range(args.steps)] for _ in range(n)]
-    ev_kv = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_kv = [[(Event(), Event())
               for _ in range(args.steps)] for _ in range(n)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        for i, (_, db) in enumerate(dbs):
+        for i, (kv_write, attention) in enumerate(calls):
             ev_kv[i][k][0].record()
-            db.kv_write()
+            kv_write()
             ev_kv[i][k][1].record()
             ev_attn[i][k][0].record()
-            db.attention()
+            attention()
             ev_attn[i][k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -154,8 +207,8 @@ def decode_rows(args, mixed):
     cpa.cpa_plan_upload(plan, ws)
     q = db.q[:nd]
     out = db.out[:nd]
-    r = median_ms(lambda: cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table,
-                                            out, ws), args.decode_reps, 5)
+    r = median_ms(cpa.bind_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws),
+                  args.decode_reps, 5)
     hkv, d = b.num_kv_heads, b.head_dim
     kv_bytes = float(sum(int(n) for n in b.seq_lens[:nd])) * hkv * d * 2 * 2
     qo_bytes = nd * b.num_q_heads * d * 2 * 2
@@ -173,14 +226,14 @@ def mixed_extras(args, mixed):
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     b, db = mixed
-    r_all = median_ms(lambda: db.attention(), args.decode_reps, 3)
+    r_all = median_ms(db.bound()[1], args.decode_reps, 3)
     nd = 16
     ql = [0] * nd + [int(x) for x in b.query_lens[nd:]]
     plan = cpa.cpa_plan_create(db.desc, ql, b.seq_lens)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     cpa.cpa_plan_upload(plan, ws)
-    r_pf = median_ms(lambda: cpa.cpa_attention(plan, db.q[nd:], db.k_cache, db.v_cache,
-                                               db.block_table, db.out[nd:], ws),
+    r_pf = median_ms(cpa.bind_attention(plan, db.q[nd:], db.k_cache, db.v_cache,
+                                        db.block_table, db.out[nd:], ws),
                      args.decode_reps, 3)
     pf_flops = sum(flops_chunk(40, 128, int(c), int(n) - int(c))
                    for c, n in zip(b.query_lens[nd:], b.seq_lens[nd:]))
@@ -225,9 +278,12 @@ def long_context(args):
         kn, vn, sm = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl]
         q, out = db.q[sl], db.out[sl]
 
+        kv_write = cpa.bind_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
+        attention = cpa.bind_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+
         def chunk():
-            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
-            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+            kv_write()
+            attention()
         r = median_ms(chunk, 10, 2)
         f = flops_chunk(64, 128, 2048, h)
         tot_f += f
@@ -258,9 +314,12 @@ def chunk_runner(db, cpa, torch):
         sl = slice(L, L + c)
         kn, vn, sm, q, out = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl], db.q[sl], db.out[sl]
 
+        kv_write = cpa.bind_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
+        attention = cpa.bind_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+
         def f():
-            cpa.cpa_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
-            cpa.cpa_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
+            kv_write()
+            attention()
         f.plan = plan
         return f
     return runner
@@ -413,7 +472,7 @@ def step_loop(requests, budget, rule, fit, seed=7, align=128):
         return torch.randn((budget, h, d), generator=g, device="cuda").to(torch.bfloat16) \
             .view(torch.int16)
     pools = (pool(hq), pool(hkv), pool(hkv))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = Event(), Event()
     steps, refused, host_s = [], 0, 0.0
     first_tok, dec_times = {}, {}
     cum = 0.0

@@ -264,6 +264,41 @@ def cpa_attention(plan: Plan, q, k_cache, v_cache, block_table, out, workspace, 
                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+# ---- calls marshalled once ---------------------------------------------------
+# Launch-bound loops (the bench's timed steps) call the same entry point on the
+# same buffers many times. These return a callable holding the marshalled
+# arguments (pointers, sizes, the stream current at bind time), so each launch
+# costs one foreign call and a status check. The tensors must outlive it.
+
+def bind_kv_write(desc, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+    args = (ctypes.byref(desc), _dev(k_new, "k_new", 2), _dev(v_new, "v_new", 2),
+            _dev(slot_mapping, "slot_mapping", 4), int(slot_mapping.shape[0]),
+            _dev(k_cache, "k_cache", 2), _dev(v_cache, "v_cache", 2), _stream(stream))
+    keep = (desc, k_new, v_new, slot_mapping, k_cache, v_cache)
+    fn = _lib.cpa_kv_write
+
+    def call(_keep=keep):
+        st = fn(*args)
+        if st != CPA_OK:
+            _check(st)
+    return call
+
+
+def bind_attention(plan: Plan, q, k_cache, v_cache, block_table, out, workspace, stream=None):
+    args = (plan.handle, _dev(q, "q", 2), _dev(k_cache, "k_cache", 2),
+            _dev(v_cache, "v_cache", 2), _dev(block_table, "block_table", 4),
+            _dev(out, "out"), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    keep = (plan, q, k_cache, v_cache, block_table, out, workspace)
+    fn = _lib.cpa_attention
+
+    def call(_keep=keep):
+        st = fn(*args)
+        if st != CPA_OK:
+            _check(st)
+    return call
+
+
 def cpa_validate_metadata(desc, slot_mapping=None, block_table=None, query_lens=None,
                           seq_lens=None) -> None:
     def opt(a):

@@ -56,6 +56,14 @@ class DeviceBatch:
         self.attention()
         torch.cuda.synchronize()
 
+    def bound(self):
+        """(kv_write, attention) with their arguments marshalled once, on the
+        current stream."""
+        return (cpa.bind_kv_write(self.desc, self.k_new, self.v_new, self.slot_mapping,
+                                  self.k_cache, self.v_cache),
+                cpa.bind_attention(self.plan, self.q, self.k_cache, self.v_cache,
+                                   self.block_table, self.out, self.workspace))
+
     def out_f64(self) -> np.ndarray:
         if self.out.dtype == torch.float32:
             return self.out.cpu().numpy().astype(np.float64)
