@@ -167,6 +167,24 @@ def test_constant_v_returns_v(H):
     assert err[100:].max() <= 1e-5      # the decode row
 
 
+def test_bound_calls_match(H):
+    """binding.bind_kv_write / bind_attention (arguments marshalled once)
+    launch the same work as the per-call entry points: bitwise equal."""
+    b = make(seed=13, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+             query_lens=[40, 1], seq_lens=[300, 90], extra_pages=1)
+    banner("bound calls")
+    db = H.DeviceBatch(b)
+    db.run()
+    first = db.out.clone()
+    db.out.fill_(0)
+    kv_write, attention = db.bound()
+    for _ in range(2):
+        kv_write()
+        attention()
+    torch.cuda.synchronize()
+    assert torch.equal(first, db.out)
+
+
 def test_attention_requires_upload(H):
     from chunked_prefill_attention_slot_amd import binding as cpa
     b = make(seed=11, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
