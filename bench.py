@@ -182,7 +182,11 @@ def headline(args):
     ms_per_step = wall * 1e3 / args.steps
     total_flops = sum(flops)
     achieved = (total_flops / n) / (attn_ms_tot / n * 1e-3) / 1e12
+    # The timed steps' outputs (bf16 bits), for the parity figure of the
+    # CPU baseline leg.
+    outs = {h: db.out.cpu().numpy().view(np.uint16).copy() for h, db in dbs}
     return {
+        "outputs": outs,
         "ms_per_step": ms_per_step,
         "value": total_flops / (ms_per_step * 1e-3) / 1e12,
         "per_H": per_h,
@@ -618,10 +622,12 @@ def alignment_study(args, hists=(0, 4096, 12288),
     return out
 
 
-def cpu_baseline(budget_s=10.0):
+def cpu_baseline(budget_s=10.0, gpu_outputs=None):
     """The fp64 oracle on host cores over the headline step: the Llama-3-8B
     chunk at H = 0, 4096, 8192, 12288, every query head, repeated until
-    budget_s seconds have passed (whole passes only)."""
+    budget_s seconds have passed (whole passes only). Its first pass is also
+    compared element by element with the outputs of the timed GPU steps
+    (gpu_outputs: H -> bf16 bits [512, 32, 128])."""
     from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
     from oracle.attention import causal_chunk_attention, gather_sequence, widen_bf16
     from oracle.kv_cache import kv_write
@@ -638,6 +644,7 @@ def cpu_baseline(budget_s=10.0):
         kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
         prepared.append((h, b, kc, vc))
     passes = 0
+    parity = {}
     t0 = time.perf_counter()
     while True:
         for h, b, kc, vc in prepared:
@@ -646,8 +653,15 @@ def cpu_baseline(budget_s=10.0):
             v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size))
             q = widen_bf16(b.q)
             for head in range(32):
-                causal_chunk_attention(q[:, head], k[:, head // 4], v[:, head // 4], h,
-                                       1.0 / math.sqrt(128))
+                o = causal_chunk_attention(q[:, head], k[:, head // 4], v[:, head // 4], h,
+                                           1.0 / math.sqrt(128))
+                if passes == 0 and gpu_outputs is not None and h in gpu_outputs:
+                    g = (gpu_outputs[h][:, head].astype(np.uint32) << 16).view(np.float32)
+                    e = np.abs(g.astype(np.float64) - o)
+                    acc = parity.setdefault(h, [0.0, 0.0, 0])
+                    acc[0] = max(acc[0], float(e.max()))
+                    acc[1] += float(e.sum())
+                    acc[2] += e.size
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -661,6 +675,15 @@ def cpu_baseline(budget_s=10.0):
            "sample": f"{passes} pass(es) of the headline step (Llama-3-8B, C=512 at H=0/4096/"
                      f"8192/12288, all 32 query heads), fp64 NumPy oracle incl. gather; {dt:.1f} s",
            "seconds": dt, "cpu_count": os.cpu_count(), "affinity": aff, "blas": blas}
+    if parity:
+        res["parity_vs_gpu"] = {
+            "note": "oracle vs the timed GPU steps' bf16 outputs, every element; bar: "
+                    "max-abs 2e-2, mean-abs 2e-3",
+            "per_H": {str(h): {"max_abs": m, "mean_abs": t / c} for h, (m, t, c) in parity.items()},
+            "max_abs": max(m for m, _, _ in parity.values()),
+            "mean_abs": sum(t for _, t, _ in parity.values()) / sum(c for _, _, c in parity.values())}
+        log(f"[bench] parity of the timed steps vs the oracle: max_abs "
+            f"{res['parity_vs_gpu']['max_abs']:.2e}, mean_abs {res['parity_vs_gpu']['mean_abs']:.2e}")
     log(f"[bench] cpu oracle: {passes} passes in {dt:.1f} s -> {res['value']*1e3:.2f} GFLOP/s")
     return res
 
@@ -763,7 +786,7 @@ def main():
         out["step_loop"] = serving_run(args)
         out["alignment"] = alignment_study(args)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(gpu_outputs=head.pop("outputs"))
     out["context_from_pages"] = {
         "note": "whole-model figures on A100 from the vLLM chunked-prefill article, "
                 "section 2.1; not this kernel, not comparable",
