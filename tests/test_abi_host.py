@@ -166,6 +166,22 @@ def test_plan_counts_and_pairs(cpa):
     assert p.info()["num_prefill_items"] == 64
 
 
+def test_plan_page_cap_splits(cpa):
+    """A tile whose key range spans more block-table entries than one
+    prefill item stages in LDS (2047) is split even when splitting is
+    turned off; every piece stays within the cap."""
+    d = desc(cpa, num_q_heads=1, num_kv_heads=1, head_dim=64, page_size=16,
+             num_blocks=3000, max_blocks_per_seq=2600)
+    n = 40000                                  # 2500 pages of 16 keys
+    p = cpa.cpa_plan_create(d, [64], [n], {"prefill_split": 1})
+    info = p.info()
+    assert info["num_prefill_items"] == 2      # 32704 keys per piece at most
+    assert info["num_combine_items"] == 1
+    assert info["num_partial_rows"] == 2 * 64
+    p = cpa.cpa_plan_create(d, [64], [32000], {"prefill_split": 1})
+    assert p.info()["num_prefill_items"] == 1  # 2000 pages: within the cap
+
+
 def test_plan_mixed_batch(cpa):
     d = desc(cpa, num_q_heads=40, num_kv_heads=40, num_blocks=1200, max_blocks_per_seq=64)
     ql = [1] * 3 + [512, 0]

@@ -113,6 +113,17 @@ def test_large_scores(H, shift):
         H.compare(db.out_f64(), ref, f"{label} {opts}")
 
 
+def test_page_cap_split(H):
+    """Maximum item size: one sequence of 40000 keys in 16-key pages (2500
+    block-table entries, over the 2047 one item stages), splitting turned
+    off, so only the cap splits the tile; every row compared."""
+    b = make(seed=14, num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=16,
+             query_lens=[64], seq_lens=[40000], extra_pages=3)
+    db = run_and_compare(H, b, "page cap split H=39936 C=64 P=16",
+                         options={"prefill_split": 1})
+    assert db.plan.info()["num_prefill_items"] == 2
+
+
 def test_forced_splits_agree(H):
     b = make(seed=7, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
              query_lens=[256], seq_lens=[3000], extra_pages=1)
