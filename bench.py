@@ -14,9 +14,11 @@ layer of a batch step). Inputs are resident in HBM before timing starts.
 
 The printed JSON line (last line of stdout) carries:
   value      -- algorithmic TFLOP/s of the whole step (KV writes included),
-                FLOP per chunk = 4*Hq*d*C*(H + C/2);
+                FLOP per chunk = 4*Hq*d*C*(H + C/2), over K steps timed
+                with no events between the launches;
   roofline   -- the attention call (prefill MFMA kernel + split combine)
-                against bf16 dense MFMA peak, averaged over the four H;
+                against bf16 dense MFMA peak, averaged over the four H, its
+                duration from HIP events in a second pass of K steps;
   decode     -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
                 40/40 heads): algorithmic K+V+Q+O bytes / time vs HBM peak;
   cpu_baseline -- the fp64 oracle on a bounded sample of the H=12288 chunk.
@@ -146,30 +148,37 @@ def headline(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Per-call events on the launch stream (torch's current stream), inside
-    # the timed region.
-    n = len(dbs)
-    ev_attn = [[(Event(), Event())
-                for _ in range(args.steps)] for _ in range(n)]
-    ev_kv = [[(Event(), Event())
-              for _ in range(args.steps)] for _ in range(n)]
-    torch.cuda.synchronize()
+    # Timed region: K steps exactly as a caller issues them. A recorded event
+    # costs 1.5-2 us of stream time (its own packet between two kernels), so
+    # none is recorded here.
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        for i, (kv_write, attention) in enumerate(calls):
-            ev_kv[i][k][0].record()
-            kv_write()
-            ev_kv[i][k][1].record()
-            ev_attn[i][k][0].record()
-            attention()
-            ev_attn[i][k][1].record()
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Per-launch durations: the same K steps again with one event before the
+    # first call and one after every call, on the launch stream (torch's
+    # current stream); each call's time is the span between the events that
+    # bracket it, so it includes its launch and one event's overhead.
+    n = len(dbs)
+    evs = [[Event() for _ in range(2 * n + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        e = evs[k]
+        e[0].record()
+        for i, (kv_write, attention) in enumerate(calls):
+            kv_write()
+            e[2 * i + 1].record()
+            attention()
+            e[2 * i + 2].record()
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t1
     per_h = []
     attn_ms_tot = 0.0
     for i, h in enumerate(args.hist):
-        a = sorted(s.elapsed_time(e) for s, e in ev_attn[i])
-        kv = sorted(s.elapsed_time(e) for s, e in ev_kv[i])
+        a = sorted(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for e in evs)
+        kv = sorted(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs)
         am = sum(a) / len(a)
         attn_ms_tot += am
         per_h.append({"H": h, "attn_us_mean": am * 1e3, "attn_us_median": a[len(a) // 2] * 1e3,
@@ -180,6 +189,8 @@ def headline(args):
             f"({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak); kv_write "
             f"{per_h[-1]['kv_write_us_mean']:.1f} us")
     ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events, "
+        f"{wall_ev*1e3/args.steps*1e3:.1f} us with {2*n+1} events")
     total_flops = sum(flops)
     achieved = (total_flops / n) / (attn_ms_tot / n * 1e-3) / 1e12
     # The timed steps' outputs (bf16 bits), for the parity figure of the
@@ -188,6 +199,7 @@ def headline(args):
     return {
         "outputs": outs,
         "ms_per_step": ms_per_step,
+        "ms_per_step_with_events": wall_ev * 1e3 / args.steps,
         "value": total_flops / (ms_per_step * 1e-3) / 1e12,
         "per_H": per_h,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -718,8 +730,8 @@ def load_traffic(kernel_src):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -755,6 +767,7 @@ def main():
                                "KV write + attention per chunk",
                    "chunk": CHUNK, "hist": list(args.hist), "page_size": 128},
         "roofline": head["roofline"], "per_H": head["per_H"],
+        "ms_per_step_with_events": head["ms_per_step_with_events"],
     }
     traffic, note = load_traffic(os.path.join(ROOT, "chunked_prefill_attention_slot_amd", "csrc",
                                               "prefill_attn.hip"))

@@ -108,7 +108,7 @@ struct cpa_plan_s {
   int32_t num_seqs = 0, num_tokens = 0;
   int32_t group = 1;             // Hq / Hkv
   int32_t decode_group = 0;      // heads per decode item, 0 if no decode kernel
-  int32_t part_rows = 0, max_combine_rows = 0;
+  int32_t part_rows = 0, max_combine_rows = 0, max_combine_splits = 0;
   int64_t visible_pairs = 0;
   std::vector<cpa::WorkItem> prefill, decode;
   std::vector<cpa::CombineItem> combine;
@@ -140,6 +140,7 @@ void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, in
   const int part0 = p->part_rows;
   p->part_rows += nsplit * rows;
   p->max_combine_rows = std::max(p->max_combine_rows, rows);
+  p->max_combine_splits = std::max(p->max_combine_splits, nsplit);
   p->combine.push_back(cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, nsplit, part0, rows, 0});
   int start = 0;
   for (int k = 0; k < nsplit; ++k) {
@@ -454,7 +455,8 @@ cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache, cons
                          (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
   if (e != hipSuccess) return cpa::hip_fail(e, "decode attention launch");
   e = cpa::launch_combine(reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine),
-                          (int)plan->combine.size(), plan->max_combine_rows, a, d.head_dim, stream);
+                          (int)plan->combine.size(), plan->max_combine_rows,
+                          plan->max_combine_splits, a, d.head_dim, stream);
   if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
   return cpa::ok();
 }

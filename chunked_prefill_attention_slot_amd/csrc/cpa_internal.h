@@ -65,9 +65,10 @@ hipError_t launch_prefill(const WorkItem* items, int num_items,
 hipError_t launch_decode(const WorkItem* items, int num_items,
                          const AttnArgs& a, int head_dim, int group,
                          hipStream_t stream);
+// max_rows / max_splits: the largest rows and nsplit over the items.
 hipError_t launch_combine(const CombineItem* items, int num_items,
-                          int max_rows, const AttnArgs& a, int head_dim,
-                          hipStream_t stream);
+                          int max_rows, int max_splits, const AttnArgs& a,
+                          int head_dim, hipStream_t stream);
 hipError_t launch_kv_write(const uint16_t* k_new, const uint16_t* v_new,
                            const int32_t* slot_mapping, int32_t num_tokens,
                            uint16_t* k_cache, uint16_t* v_cache,

@@ -256,56 +256,64 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
 }
 
 // Log-sum-exp merge of the split partials of one tile: thread -> (packed
-// row r, 4 consecutive d). Split k holds O_k/l_k, max m_k and sum l_k;
+// row r, 8 consecutive d). Split k holds O_k/l_k, max m_k and sum l_k;
 // O = sum_k 2^(m_k - m) l_k (O_k/l_k) / sum_k 2^(m_k - m) l_k, m = max_k m_k.
-template <int D, bool F32>
+// B splits are read per batch: 4 when no tile of the plan has more, else 8.
+template <int D, bool F32, int B>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
                                                       AttnArgs a) {
-  constexpr int D4 = D / 4;
-  constexpr int B = 8;  // splits read per batch
+  constexpr int D8 = D / 8;
   const CombineItem it = items[blockIdx.x];
   const int idx = blockIdx.y * 256 + threadIdx.x;
-  const int r = idx / D4, d = 4 * (idx % D4);
+  const int r = idx / D8, d = 8 * (idx % D8);
   if (r >= it.rows) return;
   // Every load of a batch is issued before any is used (indices past the
-  // last split repeat it and get weight 0), so a batch of eight splits
-  // costs one round trip to memory; earlier batches are rescaled to the
-  // running max.
+  // last split repeat it and get weight 0), so a batch costs one round trip
+  // to memory; earlier batches are rescaled to the running max. A split's
+  // (max, sum) pair is one 8-byte load, its 8 values one 16-byte load
+  // (bf16) or two (fp32).
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   float mm = -INFINITY, ll = 0.f;
-  f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
   for (int k0 = 0; k0 < it.nsplit; k0 += B) {
-    float mk[B], lk[B];
-    f32x4 ok[B];
+    float2 mlk[B];
+    f32x4 ok0[B], ok1[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int k = min(k0 + j, it.nsplit - 1);
       const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
-      mk[j] = a.part_ml[prow * 2];
-      lk[j] = a.part_ml[prow * 2 + 1];
+      mlk[j] = ml[prow];
       if constexpr (F32) {
-        ok[j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + prow * D + d);
+        const f32x4* po = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) +
+                                                          prow * D + d);
+        ok0[j] = po[0];
+        ok1[j] = po[1];
       } else {
-        const u32x2 b = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) +
+        const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) +
                                                          prow * D + d);
-        ok[j] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+        ok0[j] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+        ok1[j] = f32x4{bf16_lo(b[2]), bf16_hi(b[2]), bf16_lo(b[3]), bf16_hi(b[3])};
       }
     }
     float bm = mm;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      if (k0 + j >= it.nsplit) mk[j] = -INFINITY;
-      bm = fmaxf(bm, mk[j]);
+      if (k0 + j >= it.nsplit) mlk[j].x = -INFINITY;
+      bm = fmaxf(bm, mlk[j].x);
     }
     const float a0 = (mm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm - bm);
     ll *= a0;
-    oo *= a0;
+    o0 *= a0;
+    o1 *= a0;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       // Weight of split k: its sum l_k scaled to the common max; the stored
       // partial is O_k / l_k.
-      const float wk = (mk[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[j] - bm) * lk[j];
+      const float wk =
+          (mlk[j].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mlk[j].x - bm) * mlk[j].y;
       ll += wk;
-      oo += wk * ok[j];
+      o0 += wk * ok0[j];
+      o1 += wk * ok1[j];
     }
     mm = bm;
   }
@@ -313,10 +321,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
   const int qi = r / it.nheads, hl = r - qi * it.nheads;
   const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D + d;
   if constexpr (F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob) = oo * inv;
+    f32x4* po = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob);
+    po[0] = o0 * inv;
+    po[1] = o1 * inv;
   } else {
-    u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = o2;
+    const u32x4 o = {pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
+                     pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = o;
   }
 }
 
@@ -333,6 +344,16 @@ hipError_t launch_decode_d(const WorkItem* items, int n, const AttnArgs& a, int 
   return hipGetLastError();
 }
 
+template <int D, bool F32>
+hipError_t launch_combine_t(const CombineItem* items, dim3 grid, int max_splits,
+                            const AttnArgs& a, hipStream_t s) {
+  if (max_splits <= 4)
+    hipLaunchKernelGGL((combine_kernel<D, F32, 4>), grid, dim3(256), 0, s, items, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, F32, 8>), grid, dim3(256), 0, s, items, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const WorkItem* items, int num_items, const AttnArgs& a, int head_dim,
@@ -343,22 +364,16 @@ hipError_t launch_decode(const WorkItem* items, int num_items, const AttnArgs& a
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows,
+hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows, int max_splits,
                           const AttnArgs& a, int head_dim, hipStream_t stream) {
   if (num_items == 0) return hipSuccess;
-  const int threads = max_rows * (head_dim / 4);
+  const int threads = max_rows * (head_dim / 8);
   const dim3 grid(num_items, (threads + 255) / 256);
-  if (head_dim == 128 && a.out_f32)
-    hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(256), 0, stream, items, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(256), 0, stream, items, a);
-  else if (head_dim == 64 && a.out_f32)
-    hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(256), 0, stream, items, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(256), 0, stream, items, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (head_dim == 128 && a.out_f32) return launch_combine_t<128, true>(items, grid, max_splits, a, stream);
+  if (head_dim == 128) return launch_combine_t<128, false>(items, grid, max_splits, a, stream);
+  if (head_dim == 64 && a.out_f32) return launch_combine_t<64, true>(items, grid, max_splits, a, stream);
+  if (head_dim == 64) return launch_combine_t<64, false>(items, grid, max_splits, a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace cpa

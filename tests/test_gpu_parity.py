@@ -128,7 +128,7 @@ def test_forced_splits_agree(H):
     b = make(seed=7, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
              query_lens=[256], seq_lens=[3000], extra_pages=1)
     outs = []
-    for split in (1, 3, 7):
+    for split in (1, 3, 4, 5, 7, 9, 17):
         db = run_and_compare(H, b, f"split {split}", options={"prefill_split": split})
         outs.append(db.out_f64())
     for o in outs[1:]:
