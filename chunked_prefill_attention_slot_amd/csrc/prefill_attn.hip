@@ -604,55 +604,70 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       run(ic<1>{});
   }
 
+  // Epilogue. Every wave is past its last read of the tile buffers after
+  // this barrier; they then stage each wave's O rows, so that the global
+  // stores write whole rows (a lane of the accumulator layout holds 4
+  // values of one row, and storing from there would send every store
+  // instruction to 32 different rows).
+  __syncthreads();
   float l_tot;
   {
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                      __float_as_uint(l_run), false, false);
     l_tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
   }
-  if (!row_ok) return;
-  if (it.part < 0) {
-    const float inv = 1.f / l_tot;
-    const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D;
+  // A split item's partial is O/l in the output's precision (a row with no
+  // visible key in the range has l = 0 and stores zeros), with fp32 (m, l).
+  const bool split = it.part >= 0;
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  auto store_rows = [&](auto ec) __attribute__((always_inline)) {
+    constexpr int E = decltype(ec)::value;  // bytes per stored element
+    constexpr int RB = D * E;               // bytes per row
+    constexpr int CH = RB / 16;             // 16-byte chunks per row
+    constexpr int RPS = 64 / CH;            // rows per store instruction
+    static_assert(NW * 32 * RB <= (int)sizeof(smem), "O staging exceeds the tile buffers");
+    uint8_t* region = smem + w * 32 * RB;
+    // Lane (n, hh) holds d = 32db + 8g4 + 4hh .. +3 of row n; chunk c of
+    // row R sits at chunk c ^ (R mod CH), so neither side conflicts on banks.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * hh;
+        const int byte = (32 * db + 8 * g4 + 4 * hh) * E;
+        uint8_t* dst = region + n * RB + (((byte >> 4) ^ (n & (CH - 1))) << 4) + (byte & 15);
         const float v0 = oacc[db][4 * g4 + 0] * inv, v1 = oacc[db][4 * g4 + 1] * inv;
         const float v2 = oacc[db][4 * g4 + 2] * inv, v3 = oacc[db][4 * g4 + 3] * inv;
-        if (a.out_f32) {
-          f32x4 o4 = {v0, v1, v2, v3};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + d) = o4;
-        } else {
-          u32x2 o2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob + d) = o2;
-        }
+        if constexpr (E == 4)
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+        else
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
-  } else {
-    // Partial of a split key range: O/l in the output's precision (a row
-    // with no visible key in the range has l = 0 and stores zeros).
-    const size_t prow = (size_t)it.part + r;
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    // The wave reads back only what it wrote; LDS serves one wave's
+    // operations in order.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int lr = lane / CH, lc = lane % CH;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * hh;
-        const float v0 = oacc[db][4 * g4 + 0] * inv, v1 = oacc[db][4 * g4 + 1] * inv;
-        const float v2 = oacc[db][4 * g4 + 2] * inv, v3 = oacc[db][4 * g4 + 3] * inv;
-        if (a.out_f32) {
-          f32x4 o4 = {v0, v1, v2, v3};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + prow * D + d) = o4;
-        } else {
-          u32x2 o2 = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + prow * D + d) = o2;
-        }
+    for (int k = 0; k < 32 / RPS; ++k) {
+      const int R = k * RPS + lr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + R * RB + ((lc ^ (R & (CH - 1))) << 4));
+      const int rr = 32 * w + R;  // packed row
+      const int q = rr / it.nheads, h = rr - q * it.nheads;
+      if (q < it.nq) {
+        uint8_t* dst = split
+            ? static_cast<uint8_t*>(a.part_o) + ((size_t)it.part + rr) * RB
+            : static_cast<uint8_t*>(a.out) +
+                  ((size_t)(it.tok0 + q) * a.num_q_heads + it.head0 + h) * RB;
+        *reinterpret_cast<u32x4*>(dst + lc * 16) = v;
       }
-    if (hh == 0) {
-      a.part_ml[prow * 2 + 0] = unset ? -INFINITY : m_ref;
-      a.part_ml[prow * 2 + 1] = l_tot;
     }
+  };
+  if (a.out_f32)
+    store_rows(ic<4>{});
+  else
+    store_rows(ic<2>{});
+  if (split && hh == 0 && row_ok) {
+    float2* ml = reinterpret_cast<float2*>(a.part_ml) + it.part + r;
+    *ml = float2{unset ? -INFINITY : m_ref, l_tot};
   }
 }
 
