@@ -55,6 +55,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 16-byte chunk swizzle of staged Q row r. The eight lanes of one
+// ds_read_b128 phase read rows 0..7 at the same logical chunk; these land on
+// distinct bank groups (rows of d = 64 are half a bank cycle long).
+template <int CPR>
+__device__ __forceinline__ int q_swz(int r) {
+  if constexpr (CPR == 16) return r & 7;
+  return (r >> 1) & 3;
+}
+
 template <int D>
 struct Cfg {
   static constexpr int NW = kPrefillWaves;
@@ -162,36 +171,30 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const bool row_ok = qi < it.nq;
   const int qpos = it.hist + it.q0 + qi;
 
-  // Q fragment: B operand of K.Q^T, lane holds d = 16ks + 8hh .. +7,
-  // multiplied by scale*log2(e) and rounded to bf16, so the products are
-  // scores in log2 units (the rounding perturbs a score by far less than
-  // the bf16 rounding of the weights that follows).
-  bf16x8 qf[NKS];
+  // Q is copied into LDS first (buffers 2 and 3, which the first tile
+  // copies leave free), whole rows per DMA instruction: a direct load in
+  // the fragment layout would send each load instruction to 32 rows.
+  const uint32_t smem_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int q_region = (w < NW / 2 ? 2 * TILE : V_REGION + 2 * TILE) + (w % (NW / 2)) * 32 * ROWB;
+  static_assert((NW / 2) * 32 * ROWB <= 2 * TILE, "Q staging exceeds two tile buffers");
   {
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(
-        a.q + ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D);
-    u32x4 qv[NKS];
+    const int lrow = lane / CPR, lpc = lane % CPR;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qv[ks] = u32x4{0u, 0u, 0u, 0u};
-      if (row_ok) qv[ks] = qrow[2 * ks + hh];
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int R = k * RPI + lrow;  // row of the wave
+      const int rq = 32 * w + R;
+      const int q = rq / it.nheads, h = rq - q * it.nheads;
+      const uint16_t* src = a.zeros;
+      if (q < it.nq)
+        src = a.q + ((size_t)(it.tok0 + q) * a.num_q_heads + it.head0 + h) * D +
+              (lpc ^ q_swz<CPR>(R)) * 8;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(smem_lds + q_region + k * 1024));
     }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[j] = pack_bf16x2(__uint_as_float(qv[ks][j] << 16) * sl2e,
-                           __uint_as_float(qv[ks][j] & 0xFFFF0000u) * sl2e);
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-    // Wait for Q here (vmcnt 0): a wait the compiler would otherwise place
-    // at the first product inside the tile loop would also stall on the
-    // next tile's DMA.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-
-  // Stage the block-table entries of this item's key range.
+  bf16x8 qf[NKS];
+  // Stage the block-table entries of this item's key range (the loads
+  // overlap the Q copy).
   const int j_end = min(it.kv1, it.hist + it.q0 + it.nq);
   const int plog = a.page_log2, pmask = (1 << plog) - 1;
   const int page0 = it.kv0 >> plog;
@@ -203,6 +206,23 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       s_pages[i] = ((unsigned)pg < (unsigned)a.num_blocks) ? pg : -1;
     }
   }
+  // Q fragment: B operand of K.Q^T, lane holds d = 16ks + 8hh .. +7 of row
+  // n, multiplied by scale*log2(e) and rounded to bf16, so the products are
+  // scores in log2 units (the rounding perturbs a score by far less than
+  // the bf16 rounding of the weights that follows). The wave reads only the
+  // rows it copied.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(
+        smem + q_region + n * ROWB + (((2 * ks + hh) ^ q_swz<CPR>(n)) << 4));
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = pack_bf16x2(__uint_as_float(qv[j] << 16) * sl2e,
+                         __uint_as_float(qv[j] & 0xFFFF0000u) * sl2e);
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
   __syncthreads();
 
   // DMA of one tile: wave w issues instructions w*IPW + u of each matrix;
@@ -211,8 +231,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   // page number is one uniform value per wave, looked up ahead of the copy.
   static_assert(IPW * RPI <= 16, "a wave's rows must fit the smallest page");
   const int lrow = lane / CPR, lpc = lane % CPR;
-  const uint32_t smem_lds =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // Block-table entry of this wave's rows of the tile at key j0, read from
   // the staged copy; -1 past the key range. page_of makes it uniform. In the
   // tile loop the entry is read one copy ahead, so the read's latency (it
