@@ -661,7 +661,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
     // The wave reads back only what it wrote; LDS serves one wave's
-    // operations in order.
+    // operations in order. The rows go out as streaming stores (nothing in
+    // this launch reads them again).
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int lr = lane / CH, lc = lane % CH;
 #pragma unroll
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
             ? static_cast<uint8_t*>(a.part_o) + ((size_t)it.part + rr) * RB
             : static_cast<uint8_t*>(a.out) +
                   ((size_t)(it.tok0 + q) * a.num_q_heads + it.head0 + h) * RB;
-        *reinterpret_cast<u32x4*>(dst + lc * 16) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + lc * 16));
       }
     }
   };
