@@ -16,7 +16,8 @@ The printed JSON line (last line of stdout) carries:
   value      -- algorithmic TFLOP/s of the whole step (KV writes included),
                 FLOP per chunk = 4*Hq*d*C*(H + C/2), over K steps timed
                 with no events between the launches;
-  roofline   -- the attention call (prefill MFMA kernel + split combine)
+  roofline   -- the step's call (cpa_kv_write_attention: the prefill MFMA
+                kernel with the KV write inside, then the split combine)
                 against bf16 dense MFMA peak, averaged over the four H, its
                 duration from HIP events in a second pass of K steps;
   decode     -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
@@ -137,16 +138,25 @@ def headline(args):
     flops = [flops_chunk(hq, d, CHUNK, h) for h in args.hist]
 
     # Each call's arguments are marshalled once (binding.bind_*): the timed
-    # loop then costs one foreign call per launch on the host.
+    # loop then costs one foreign call per launch on the host. A step issues
+    # cpa_kv_write_attention per chunk (the KV write inside the attention
+    # launch); the same step through the two separate calls, cpa_kv_write
+    # then cpa_attention, is timed beside it.
     calls = [db.bound() for _, db in dbs]
+    fused = [db.bound_fused() for _, db in dbs]
 
     def step():
+        for f in fused:
+            f()
+
+    def step_separate():
         for kv_write, attention in calls:
             kv_write()
             attention()
 
     for _ in range(args.warmup):
         step()
+        step_separate()
     torch.cuda.synchronize()
     # Timed region: K steps exactly as a caller issues them. A recorded event
     # costs 1.5-2 us of stream time (its own packet between two kernels), so
@@ -156,16 +166,31 @@ def headline(args):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_separate()
+    torch.cuda.synchronize()
+    wall_sep = time.perf_counter() - t0
     # Per-launch durations: the same K steps again with one event before the
     # first call and one after every call, on the launch stream (torch's
     # current stream); each call's time is the span between the events that
     # bracket it, so it includes its launch and one event's overhead.
     n = len(dbs)
-    evs = [[Event() for _ in range(2 * n + 1)] for _ in range(args.steps)]
+    evs = [[Event() for _ in range(n + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for k in range(args.steps):
         e = evs[k]
+        e[0].record()
+        for i, f in enumerate(fused):
+            f()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t1
+    evs_sep = [[Event() for _ in range(2 * n + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        e = evs_sep[k]
         e[0].record()
         for i, (kv_write, attention) in enumerate(calls):
             kv_write()
@@ -173,26 +198,28 @@ def headline(args):
             attention()
             e[2 * i + 2].record()
     torch.cuda.synchronize()
-    wall_ev = time.perf_counter() - t1
     per_h = []
-    attn_ms_tot = 0.0
+    call_ms_tot = 0.0
     for i, h in enumerate(args.hist):
-        a = sorted(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for e in evs)
-        kv = sorted(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs)
-        am = sum(a) / len(a)
-        attn_ms_tot += am
-        per_h.append({"H": h, "attn_us_mean": am * 1e3, "attn_us_median": a[len(a) // 2] * 1e3,
+        c = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        a = sorted(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for e in evs_sep)
+        kv = sorted(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs_sep)
+        cm = sum(c) / len(c)
+        call_ms_tot += cm
+        per_h.append({"H": h, "call_us_mean": cm * 1e3, "call_us_median": c[len(c) // 2] * 1e3,
+                      "attn_us_mean": sum(a) / len(a) * 1e3,
                       "kv_write_us_mean": sum(kv) / len(kv) * 1e3,
-                      "tflops": flops[i] / (am * 1e-3) / 1e12,
-                      "mfma_frac": flops[i] / (am * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
-        log(f"[bench] H={h}: attention {am*1e3:.1f} us -> {per_h[-1]['tflops']:.1f} TFLOP/s "
-            f"({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak); kv_write "
-            f"{per_h[-1]['kv_write_us_mean']:.1f} us")
+                      "tflops": flops[i] / (cm * 1e-3) / 1e12,
+                      "mfma_frac": flops[i] / (cm * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+        log(f"[bench] H={h}: kv_write_attention {cm*1e3:.1f} us -> {per_h[-1]['tflops']:.1f} "
+            f"TFLOP/s ({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak); separate calls: "
+            f"kv_write {per_h[-1]['kv_write_us_mean']:.1f} us + attention "
+            f"{per_h[-1]['attn_us_mean']:.1f} us")
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events, "
-        f"{wall_ev*1e3/args.steps*1e3:.1f} us with {2*n+1} events")
+    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events ({wall_ev*1e6/args.steps:.1f} us "
+        f"with {n+1} events); separate calls {wall_sep*1e6/args.steps:.1f} us")
     total_flops = sum(flops)
-    achieved = (total_flops / n) / (attn_ms_tot / n * 1e-3) / 1e12
+    achieved = (total_flops / n) / (call_ms_tot / n * 1e-3) / 1e12
     # The timed steps' outputs (bf16 bits), for the parity figure of the
     # CPU baseline leg.
     outs = {h: db.out.cpu().numpy().view(np.uint16).copy() for h, db in dbs}
@@ -200,12 +227,14 @@ def headline(args):
         "outputs": outs,
         "ms_per_step": ms_per_step,
         "ms_per_step_with_events": wall_ev * 1e3 / args.steps,
+        "ms_per_step_separate_calls": wall_sep * 1e3 / args.steps,
         "value": total_flops / (ms_per_step * 1e-3) / 1e12,
         "per_H": per_h,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None,
-                     "kernel": "cpa_attention (prefill_kernel<128> + combine_kernel<128>)",
+                     "kernel": "cpa_kv_write_attention (prefill_kernel<128, fused> + "
+                               "combine_kernel<128>)",
                      "flop_per_launch": total_flops / n},
     }
 
@@ -764,10 +793,12 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Llama-3-8B attention layer (32 q / 8 kv heads, d=128), "
                                "page 128, one 512-token chunk at each H in 0/4096/8192/12288; "
-                               "KV write + attention per chunk",
+                               "KV write + attention per chunk in one call "
+                               "(cpa_kv_write_attention)",
                    "chunk": CHUNK, "hist": list(args.hist), "page_size": 128},
         "roofline": head["roofline"], "per_H": head["per_H"],
         "ms_per_step_with_events": head["ms_per_step_with_events"],
+        "ms_per_step_separate_calls": head["ms_per_step_separate_calls"],
     }
     traffic, note = load_traffic(os.path.join(ROOT, "chunked_prefill_attention_slot_amd", "csrc",
                                               "prefill_attn.hip"))

@@ -209,6 +209,103 @@ void order_for_xcds(std::vector<cpa::WorkItem>& v, int nxcd) {
 
 }  // namespace
 
+namespace {
+
+// The step's new K/V rows for the fused entry point.
+struct NewRows {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+};
+
+cpa_status attention_impl(cpa_plan plan, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream, const NewRows* nr) {
+  if (!plan) return cpa::fail(CPA_ERR_INVALID_ARG, "attention: plan is NULL");
+  if (plan->num_tokens == 0) return cpa::ok();
+  if (!q || !k_cache || !v_cache || !block_table || !out || !workspace)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "attention: NULL pointer");
+  if (nr && (!nr->k_new || !nr->v_new || !nr->slot_mapping))
+    return cpa::fail(CPA_ERR_INVALID_ARG, "kv_write_attention: NULL pointer");
+  if (workspace_bytes < plan->ws_bytes)
+    return cpa::fail(CPA_ERR_WORKSPACE, "attention: workspace smaller than the plan needs");
+  {
+    std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
+    auto it = cpa::g_ws_owner.find(workspace);
+    if (it == cpa::g_ws_owner.end() || it->second != plan->id)
+      return cpa::fail(CPA_ERR_WORKSPACE,
+                       "attention: this plan was not uploaded to this workspace "
+                       "(call cpa_plan_upload first)");
+  }
+  const cpa_layer_desc& d = plan->desc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  cpa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.bt_stride = d.max_blocks_per_seq;
+  a.num_q_heads = d.num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.page_log2 = cpa::log2_exact(d.page_size);
+  a.num_blocks = d.num_blocks;
+  a.scale_log2e = d.scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
+  a.part_o = ws + plan->off_part_o;
+  a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
+  a.zeros = reinterpret_cast<const uint16_t*>(ws);
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.slot_mapping = nullptr;
+  a.k_cache_w = nullptr;
+  a.v_cache_w = nullptr;
+  a.num_new_tokens = 0;
+
+  hipError_t e = hipSuccess;
+  bool fused = false;
+  if (nr) {
+    // The prefill kernel takes the cache writes when its threads can hold
+    // them (each writes at most kFusedWritesPerThread rows' chunks);
+    // otherwise, or without prefill items, the KV-write kernel runs first.
+    const int64_t chunks = (int64_t)plan->num_tokens * d.num_kv_heads * (d.head_dim / 8);
+    const int64_t room = (int64_t)plan->prefill.size() * 64 * cpa::kPrefillWaves *
+                         cpa::kFusedWritesPerThread;
+    // (The kernel indexes the chunks in 32 bits.)
+    fused = !plan->prefill.empty() && chunks <= room && room < ((int64_t)1 << 31);
+    if (fused) {
+      a.k_new = static_cast<const uint16_t*>(nr->k_new);
+      a.v_new = static_cast<const uint16_t*>(nr->v_new);
+      a.slot_mapping = nr->slot_mapping;
+      a.k_cache_w = static_cast<uint16_t*>(nr->k_cache);
+      a.v_cache_w = static_cast<uint16_t*>(nr->v_cache);
+      a.num_new_tokens = plan->num_tokens;
+    } else {
+      e = cpa::launch_kv_write(static_cast<const uint16_t*>(nr->k_new),
+                               static_cast<const uint16_t*>(nr->v_new), nr->slot_mapping,
+                               plan->num_tokens, static_cast<uint16_t*>(nr->k_cache),
+                               static_cast<uint16_t*>(nr->v_cache), d.num_kv_heads, d.head_dim,
+                               a.page_log2, d.num_blocks, stream);
+      if (e != hipSuccess) return cpa::hip_fail(e, "kv_write launch");
+    }
+  }
+  e = cpa::launch_prefill(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_prefill),
+                          (int)plan->prefill.size(), a, d.head_dim, fused, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "prefill attention launch");
+  e = cpa::launch_decode(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_decode),
+                         (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "decode attention launch");
+  e = cpa::launch_combine(reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine),
+                          (int)plan->combine.size(), plan->max_combine_rows,
+                          plan->max_combine_splits, a, d.head_dim, stream);
+  if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
+  return cpa::ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* cpa_last_error(void) { return cpa::last_error().c_str(); }
@@ -414,51 +511,17 @@ cpa_status cpa_plan_upload(cpa_plan plan, void* workspace, size_t workspace_byte
 cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, void* out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  if (!plan) return cpa::fail(CPA_ERR_INVALID_ARG, "attention: plan is NULL");
-  if (plan->num_tokens == 0) return cpa::ok();
-  if (!q || !k_cache || !v_cache || !block_table || !out || !workspace)
-    return cpa::fail(CPA_ERR_INVALID_ARG, "attention: NULL pointer");
-  if (workspace_bytes < plan->ws_bytes)
-    return cpa::fail(CPA_ERR_WORKSPACE, "attention: workspace smaller than the plan needs");
-  {
-    std::lock_guard<std::mutex> lk(cpa::g_ws_mu);
-    auto it = cpa::g_ws_owner.find(workspace);
-    if (it == cpa::g_ws_owner.end() || it->second != plan->id)
-      return cpa::fail(CPA_ERR_WORKSPACE,
-                       "attention: this plan was not uploaded to this workspace "
-                       "(call cpa_plan_upload first)");
-  }
-  const cpa_layer_desc& d = plan->desc;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  cpa::AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.block_table = block_table;
-  a.bt_stride = d.max_blocks_per_seq;
-  a.num_q_heads = d.num_q_heads;
-  a.num_kv_heads = d.num_kv_heads;
-  a.page_log2 = cpa::log2_exact(d.page_size);
-  a.num_blocks = d.num_blocks;
-  a.scale_log2e = d.scale * 1.4426950408889634f;
-  a.out = out;
-  a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
-  a.part_o = ws + plan->off_part_o;
-  a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
-  a.zeros = reinterpret_cast<const uint16_t*>(ws);
+  return attention_impl(plan, q, k_cache, v_cache, block_table, out, workspace, workspace_bytes,
+                        stream, nullptr);
+}
 
-  hipError_t e = cpa::launch_prefill(
-      reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_prefill), (int)plan->prefill.size(), a,
-      d.head_dim, stream);
-  if (e != hipSuccess) return cpa::hip_fail(e, "prefill attention launch");
-  e = cpa::launch_decode(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_decode),
-                         (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
-  if (e != hipSuccess) return cpa::hip_fail(e, "decode attention launch");
-  e = cpa::launch_combine(reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine),
-                          (int)plan->combine.size(), plan->max_combine_rows,
-                          plan->max_combine_splits, a, d.head_dim, stream);
-  if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
-  return cpa::ok();
+cpa_status cpa_kv_write_attention(cpa_plan plan, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping, void* k_cache,
+                                  void* v_cache, const int32_t* block_table, void* out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const NewRows nr{k_new, v_new, slot_mapping, k_cache, v_cache};
+  return attention_impl(plan, q, k_cache, v_cache, block_table, out, workspace, workspace_bytes,
+                        stream, &nr);
 }
 
 cpa_status cpa_validate_metadata(const cpa_layer_desc* desc, const int32_t* slot_mapping,

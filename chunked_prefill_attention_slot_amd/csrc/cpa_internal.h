@@ -48,6 +48,15 @@ struct AttnArgs {
   void* part_o;             // [rows, d] split partials O/l: bf16 if out is bf16, else fp32
   float* part_ml;           // [rows, 2] fp32: max (log2 units), sum
   const uint16_t* zeros;    // >= 16 zero bytes: source for keys past a range
+  // Fused KV write (prefill kernel only): the step's new K/V rows, their
+  // slots and the cache they go to. Keys at positions >= hist of a sequence
+  // are then read from k_new / v_new rather than from the cache.
+  const uint16_t* k_new;    // [T, Hkv, d] bf16
+  const uint16_t* v_new;
+  const int32_t* slot_mapping;  // [T]
+  uint16_t* k_cache_w;      // the same buffers as k_cache / v_cache
+  uint16_t* v_cache_w;
+  int32_t num_new_tokens;
 };
 
 // Prefill work items: 8 waves of 32 packed rows (query x head) each.
@@ -60,8 +69,14 @@ constexpr int kSplitAlign = 64;
 // Bytes of zeros at the start of the workspace.
 constexpr int kZeroBytes = 256;
 
+// Cache rows one fused prefill thread writes at most (K and V).
+constexpr int kFusedWritesPerThread = 4;
+
+// fused: also write the step's new K/V rows into the cache (the AttnArgs
+// k_new .. num_new_tokens fields), reading new keys from k_new / v_new.
 hipError_t launch_prefill(const WorkItem* items, int num_items,
-                          const AttnArgs& a, int head_dim, hipStream_t stream);
+                          const AttnArgs& a, int head_dim, bool fused,
+                          hipStream_t stream);
 hipError_t launch_decode(const WorkItem* items, int num_items,
                          const AttnArgs& a, int head_dim, int group,
                          hipStream_t stream);

@@ -146,7 +146,7 @@ __device__ __forceinline__ int v_swz(int r) {
   return (r & 3) << 1;
 }
 
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     const WorkItem* __restrict__ items, AttnArgs a) {
   using C = Cfg<D>;
@@ -193,6 +193,29 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     }
   }
   bf16x8 qf[NKS];
+  // Fused KV write: this workgroup's share of the step's new rows (16-byte
+  // chunks idx = (blockIdx + k*gridDim)*threads + tid, below 2^31: the host
+  // fuses only then), loaded now and stored once the prologue's loads have
+  // landed. Nothing in this launch reads them from the cache: keys at
+  // positions >= hist come from k_new and v_new.
+  constexpr int KVW = FUSED ? kFusedWritesPerThread : 0;
+  u32x4 kw_k[KVW > 0 ? KVW : 1], kw_v[KVW > 0 ? KVW : 1];
+  int32_t kw_slot[KVW > 0 ? KVW : 1];
+  constexpr int CPT = D / 8;  // 16-byte chunks per head row
+  const int64_t kw_per_tok = (int64_t)a.num_kv_heads * CPT;
+  const int64_t kw_total = kw_per_tok * a.num_new_tokens;
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int k = 0; k < KVW; ++k) {
+      const uint32_t idx = (blockIdx.x + k * gridDim.x) * (64 * NW) + tid;
+      kw_slot[k] = -1;
+      if (idx < (uint32_t)kw_total) {
+        kw_slot[k] = a.slot_mapping[idx / (uint32_t)kw_per_tok];
+        kw_k[k] = reinterpret_cast<const u32x4*>(a.k_new)[idx];
+        kw_v[k] = reinterpret_cast<const u32x4*>(a.v_new)[idx];
+      }
+    }
+  }
   // Stage the block-table entries of this item's key range (the loads
   // overlap the Q copy).
   const int j_end = min(it.kv1, it.hist + it.q0 + it.nq);
@@ -212,6 +235,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   // the bf16 rounding of the weights that follows). The wave reads only the
   // rows it copied.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (FUSED) {
+    const int64_t num_slots = (int64_t)a.num_blocks << a.page_log2;
+#pragma unroll
+    for (int k = 0; k < KVW; ++k) {
+      const uint32_t idx = (blockIdx.x + k * gridDim.x) * (64 * NW) + tid;
+      const int32_t slot = kw_slot[k];
+      if (idx < (uint32_t)kw_total && slot >= 0 && slot < num_slots) {
+        const uint32_t rem = idx % (uint32_t)kw_per_tok;  // h * CPT + c
+        const uint32_t h = rem / CPT, c = rem % CPT;
+        const int64_t page = slot >> a.page_log2, off = slot & ((1 << a.page_log2) - 1);
+        const int64_t dst = (((page * a.num_kv_heads + h) << a.page_log2) + off) * CPT + c;
+        reinterpret_cast<u32x4*>(a.k_cache_w)[dst] = kw_k[k];
+        reinterpret_cast<u32x4*>(a.v_cache_w)[dst] = kw_v[k];
+      }
+    }
+  }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const u32x4 qv = *reinterpret_cast<const u32x4*>(
@@ -251,13 +290,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     koff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ k_swz<CPR>(row)) * 8) * 2);
     voff[u] = (uint32_t)(((u * RPI + lrow) * D + (lpc ^ v_swz<CPR>(row)) * 8) * 2);
   }
+  // Extra per-lane byte offset of a new-key row in k_new / v_new, whose rows
+  // are Hkv*d elements apart instead of d.
+  const uint32_t new_xoff = FUSED ? (uint32_t)(lrow * (a.num_kv_heads - 1) * D * 2) : 0u;
   // PARTS selects the matrices copied: 1 = K, 2 = V, 3 = both.
   auto issue = [&](int j0, int pg, int buf, auto parts) __attribute__((always_inline)) {
     constexpr int PARTS = decltype(parts)::value;
     const uint32_t kbuf = smem_lds + buf * TILE;
     const uint32_t vbuf = smem_lds + V_REGION + buf * TILE;
     const int key_w = j0 + w * IPW * RPI;
-    if (pg >= 0 && key_w + IPW * RPI <= j_end) {
+    // Rows read from the cache end at j_end, or (fused) at the first new key.
+    const int lim_c = FUSED ? min(j_end, it.hist) : j_end;
+    if (pg >= 0 && key_w + IPW * RPI <= lim_c) {
       // All rows of this wave are in range: uniform page base in SGPRs.
       const size_t e0 = ((((size_t)pg * a.num_kv_heads + it.kvh) << plog) + (key_w & pmask)) * D;
 #pragma unroll
@@ -268,8 +312,27 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       }
       return;
     }
-    // Last tile of the range (or an invalid block-table entry): rows past
-    // j_end read a zero block, so masked keys meet finite values.
+    if constexpr (FUSED) {
+      if (key_w >= it.hist && key_w + IPW * RPI <= j_end) {
+        // All rows are this step's new keys: row key of the sequence is
+        // token tok0 - q0 + key - hist of k_new, Hkv*d elements apart. The
+        // row offsets within one DMA instruction are per lane (koff + the
+        // extra stride), those between instructions uniform.
+        const size_t e0 =
+            ((size_t)(it.tok0 - it.q0 + key_w - it.hist) * a.num_kv_heads + it.kvh) * D;
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+          const int i = w * IPW + u;
+          const size_t eu = e0 + (size_t)u * RPI * (a.num_kv_heads - 1) * D;
+          if constexpr (PARTS & 1) lds_dma16_s(a.k_new + eu, koff[u] + new_xoff, kbuf + i * 1024);
+          if constexpr (PARTS & 2) lds_dma16_s(a.v_new + eu, voff[u] + new_xoff, vbuf + i * 1024);
+        }
+        return;
+      }
+    }
+    // Last tile of the range, a wave straddling the first new key, or an
+    // invalid block-table entry: per-lane sources; rows past j_end read a
+    // zero block, so masked keys meet finite values.
     const size_t pbase = ((size_t)(pg < 0 ? 0 : pg) * a.num_kv_heads + it.kvh) << plog;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
@@ -278,7 +341,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       const int key = j0 + row;
       const uint16_t* ks = a.zeros;
       const uint16_t* vs = a.zeros;
-      if (key < j_end && pg >= 0) {
+      if (FUSED && key < j_end && key >= it.hist) {
+        const size_t base =
+            ((size_t)(it.tok0 - it.q0 + key - it.hist) * a.num_kv_heads + it.kvh) * D;
+        ks = a.k_new + base + (lpc ^ k_swz<CPR>(row)) * 8;
+        vs = a.v_new + base + (lpc ^ v_swz<CPR>(row)) * 8;
+      } else if (key < j_end && pg >= 0) {
         const size_t base = (pbase + (key & pmask)) * D;
         ks = a.k_cache + base + (lpc ^ k_swz<CPR>(row)) * 8;
         vs = a.v_cache + base + (lpc ^ v_swz<CPR>(row)) * 8;
@@ -693,13 +761,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 }  // namespace
 
 hipError_t launch_prefill(const WorkItem* items, int num_items, const AttnArgs& a,
-                          int head_dim, hipStream_t stream) {
+                          int head_dim, bool fused, hipStream_t stream) {
   if (num_items == 0) return hipSuccess;
   const dim3 block(64 * kPrefillWaves);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(num_items), block, 0, stream, items, a);
+  if (head_dim == 128 && fused)
+    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(num_items), block, 0, stream, items, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(num_items), block, 0, stream, items, a);
+  else if (head_dim == 64 && fused)
+    hipLaunchKernelGGL((prefill_kernel<64, true>), dim3(num_items), block, 0, stream, items, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(num_items), block, 0, stream, items, a);
+    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3(num_items), block, 0, stream, items, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

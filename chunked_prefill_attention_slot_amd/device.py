@@ -56,6 +56,19 @@ class DeviceBatch:
         self.attention()
         torch.cuda.synchronize()
 
+    def kv_write_attention(self):
+        """The fused call: the same results as kv_write() then attention()."""
+        cpa.cpa_kv_write_attention(self.plan, self.q, self.k_new, self.v_new,
+                                   self.slot_mapping, self.k_cache, self.v_cache,
+                                   self.block_table, self.out, self.workspace)
+
+    def bound_fused(self):
+        """kv_write_attention with its arguments marshalled once, on the
+        current stream."""
+        return cpa.bind_kv_write_attention(self.plan, self.q, self.k_new, self.v_new,
+                                           self.slot_mapping, self.k_cache, self.v_cache,
+                                           self.block_table, self.out, self.workspace)
+
     def bound(self):
         """(kv_write, attention) with their arguments marshalled once, on the
         current stream."""

@@ -189,6 +189,34 @@ cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache,
                          hipStream_t stream);
 
 /*
+ * One batch step's KV write and attention in one call: the results (out
+ * and both caches) are those of cpa_kv_write(desc, k_new, v_new,
+ * slot_mapping, T, k_cache, v_cache) followed by cpa_attention(plan, q,
+ * k_cache, v_cache, block_table, ...), with T the plan's token count
+ * ([DS] section 3.1: slot_mapping places every new token's K/V in the
+ * cache; [CP] section 3.2.1: attention over cached and new keys).
+ * Fusing the two is this library's design, not the pages'.
+ * The prefill kernel writes the new rows itself and reads every key at a
+ * position >= H_s of its sequence from k_new / v_new instead of the cache,
+ * so the write and the reads need no ordering and the separate write
+ * launch disappears; decode rows read the cache in a later kernel. The
+ * equality therefore assumes consistent metadata: every new token's slot
+ * is block_table[s, p/P]*P + p%P for its position p (cpa_validate_metadata
+ * checks bounds, not this). Without prefill items, or when the step has
+ * more new rows than its prefill threads take, the KV-write kernel runs
+ * first and the attention follows as in cpa_attention.
+ *   k_new, v_new: device [T, Hkv, d] bf16. slot_mapping: device [T] int32.
+ *   Other arguments, layouts, ownership and errors as cpa_kv_write and
+ *   cpa_attention; a NULL pointer gives CPA_ERR_INVALID_ARG.
+ */
+cpa_status cpa_kv_write_attention(cpa_plan plan, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping,
+                                  void* k_cache, void* v_cache,
+                                  const int32_t* block_table, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
  * Host-side bounds check of metadata before it is trusted on the device:
  * every slot_mapping entry is < 0 or < NB*P and no slot repeats; every
  * block_table entry a sequence can reach (j < ceil(seq_len/P)) is in

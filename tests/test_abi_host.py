@@ -393,3 +393,23 @@ def test_scheduler_capacity_and_protocol(cpa):
         cpa.Sched(cpa.sched_cfg(0))
     with pytest.raises(cpa.CpaError):
         cpa.Sched(cpa.sched_cfg(64, cpa.CPA_RULE_PROGRESSIVE, sizes=()))
+
+
+def test_fused_call_rejects_null_pointers(cpa):
+    """cpa_kv_write_attention checks its pointers on the host before any GPU
+    work: a NULL plan or a NULL new-row pointer is CPA_ERR_INVALID_ARG (the
+    other pointers are never dereferenced on the host)."""
+    import ctypes
+    fake = ctypes.c_void_p(256)
+    p = cpa.cpa_plan_create(desc(cpa), [4], [10])
+    lib = cpa._lib
+    assert lib.cpa_kv_write_attention(None, fake, fake, fake, fake, fake, fake, fake, fake,
+                                      fake, 1 << 20, None) == cpa.CPA_ERR_INVALID_ARG
+    for hole in range(3):          # k_new, v_new, slot_mapping
+        args = [fake, fake, fake]
+        args[hole] = None
+        st = lib.cpa_kv_write_attention(p.handle, fake, *args, fake, fake, fake, fake, fake,
+                                        1 << 20, None)
+        assert st == cpa.CPA_ERR_INVALID_ARG, hole
+        assert "NULL" in cpa.cpa_last_error()
+    p.destroy()
