@@ -28,6 +28,13 @@ CASES = {
     # d = 64, MHA, a long chunk over a short prefix
     "d64": dict(seed=23, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
                 query_lens=[64, 100], seq_lens=[256, 100], extra_pages=2),
+    # the largest page (1024 keys) with GQA 32/8 and a prefix inside a page
+    "p1024": dict(seed=26, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=1024,
+                  query_lens=[300], seq_lens=[2500], extra_pages=1,
+                  rows={0: [0, 1, 100, 255, 256, 299]}),
+    # d = 64 with GQA 8/2, 32-token pages, prefixes 1 and 61
+    "d64_gqa": dict(seed=27, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+                    query_lens=[90, 3], seq_lens=[91, 64], extra_pages=2),
     # decode rows only: no prefill items, the write kernel runs first
     "decode_only": dict(seed=24, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
                         query_lens=[1, 1, 1], seq_lens=[500, 33, 1000]),
