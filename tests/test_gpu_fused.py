@@ -14,9 +14,11 @@ WRITES_PER_THREAD = 4
 THREADS_PER_ITEM = 512
 
 CASES = {
-    # one Llama-3-8B chunk at H = 0 and H = 4096 (fused)
+    # the bench's step: one Llama-3-8B chunk at each H of the sweep (fused)
     "llama3_8b_H0": dict(llama3_hist=0),
     "llama3_8b_H4096": dict(llama3_hist=4096, rows={0: [0, 1, 63, 64, 255, 256, 400, 511]}),
+    "llama3_8b_H8192": dict(llama3_hist=8192, rows={0: [0, 64, 300, 511]}),
+    "llama3_8b_H12288": dict(llama3_hist=12288, rows={0: [0, 1, 255, 511]}),
     # GQA 8/2, 16-token pages; prefixes 230 and 195 are not multiples of a
     # wave's 8 rows, so waves straddle the first new key; a decode row and a
     # fresh sequence beside them
