@@ -503,7 +503,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   // byte offset vbase) and S^T = K.Q^T for the current tile (K in buffer
   // KB), all on the matrix core. The two score chains and the four O chains
   // are independent, so products issue back to back with the LDS reads
-  // running ahead of them.
+  // running ahead of them. All 16 PV products go first, then the 16 S
+  // products: measured ~1.4% faster per step than alternating the two kinds.
   // The first phase of an item has no previous tile (S only) and the last
   // no current tile (PV only).
   auto x_phase = [&](int vbase, auto kbc, auto pvc, auto sc_) __attribute__((always_inline)) {
@@ -521,6 +522,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         const bf16x8 av = v_read(vofs[db] + vbase + 16 * hb * ROWB);
         oacc[db] = mfma32(av, pw[hb], oacc[db]);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < NKB * NKS; ++i) {
       if constexpr (S) {
         const int kb = i % NKB, ks = i / NKB;
         const bf16x8 av =
@@ -535,9 +539,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     if constexpr (PV && S) {
       __builtin_amdgcn_sched_group_barrier(0x0100, 6, 0);    // DS read
 #pragma unroll
-      for (int i = 0; i < NKB * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);  // one PV, one S product
-        if (i + 2 < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);
+      for (int i = 0; i < 2 * NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+        // two transposed V reads per PV product, then one K read per S
+        // product, issued ahead of their products
+        if (i < NKB * NKS) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+        else if (i < 2 * NKB * NKS - 4) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
       }
     } else if constexpr (S) {
       __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
