@@ -3,10 +3,7 @@ dual-stream article, section 3.1): worked cases computed by hand from the
 section's rules, an exhaustive search over all boundaries, the threshold
 edges, and the invariant that attention over the two micro-batches equals
 attention over the whole batch (the oracle's attention is per sequence)."""
-import itertools
-
 import numpy as np
-import pytest
 
 from oracle import split as sp
 from oracle.attention import paged_attention
