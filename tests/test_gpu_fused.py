@@ -19,6 +19,8 @@ CASES = {
     "llama3_8b_H4096": dict(llama3_hist=4096, rows={0: [0, 1, 63, 64, 255, 256, 400, 511]}),
     "llama3_8b_H8192": dict(llama3_hist=8192, rows={0: [0, 64, 300, 511]}),
     "llama3_8b_H12288": dict(llama3_hist=12288, rows={0: [0, 1, 255, 511]}),
+    # split tiles with fp32 output (fp32 partials)
+    "llama3_8b_H4096_f32": dict(llama3_hist=4096, out_dtype=1, rows={0: [0, 2, 200, 511]}),
     # GQA 8/2, 16-token pages; prefixes 230 and 195 are not multiples of a
     # wave's 8 rows, so waves straddle the first new key; a decode row and a
     # fresh sequence beside them
