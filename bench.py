@@ -741,17 +741,28 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
 
 
+def kernel_source_digest(path):
+    """sha256[:16] of a HIP source with its comments and whitespace removed:
+    it changes when the code does, not when only a comment does."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def load_traffic(kernel_src):
     """HBM bytes per launch of the prefill kernel from the committed counter
-    summary, or None if it was taken on a different kernel source."""
-    import hashlib
+    summary, or None if it was taken on different kernel code."""
     path = os.path.join(ROOT, "profiles", "prefill_attn_llama3_8b_c512_traffic.txt")
     try:
         fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
     except OSError:
         return None, "no counter summary"
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_16", "").strip() != sha:
+    sha = kernel_source_digest(kernel_src)
+    if fields.get("kernel_code_digest", "").strip() != sha:
         return None, "kernel changed since the counters were taken"
     return float(fields["hbm_bytes_per_launch"]), fields.get("note", "").strip()
 

@@ -2,7 +2,8 @@
 //
 // What it computes: the vLLM "Chunked-Prefills" article, section 3.2.1 --
 // a chunk's queries attend over the cached keys/values concatenated with
-// the chunk's own (all already in the paged cache), scores scaled and
+// the chunk's own (in the paged cache, or read from the step's new rows in
+// the fused mode below), scores scaled and
 // softmaxed over keys, then a weighted sum of values -- with the causal
 // mask offset by the prefix length H (query row i sits at absolute position
 // H+i and sees keys 0..H+i), and the paged-cache metadata of the Ascend
@@ -15,7 +16,7 @@
 //   * K and V rows ([key][d], as in the cache pages) are copied straight
 //     from HBM into LDS with global_load_lds_dwordx4 (no register staging),
 //     gathered through the block-table entries the item touches (staged in
-//     LDS once), over three buffers: tile t+2 is in flight while t is used;
+//     LDS once), over four buffers: tile t+2 is in flight while t is used;
 //     16-byte chunks are XOR-swizzled per row to keep the reads below free
 //     of bank conflicts;
 //   * S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS,
@@ -34,6 +35,11 @@
 //   * O^T += V^T.P^T on the same MFMA; the V^T operand comes from the [key][d]
 //     tile with ds_read_b64_tr_b16, which hands each lane four consecutive
 //     keys of one d column.
+// Q enters and O leaves through LDS (the free tile buffers), so that the
+// HBM accesses move whole rows. In the fused mode (FUSED) the kernel also
+// writes the step's new K/V rows into the cache and reads every key at a
+// position >= H from those rows instead, so no read depends on a write in
+// the same launch.
 // The rows of K fed to the first product are the tile's keys with bits 2
 // and 3 of the index swapped; that makes each lane's eight accumulators of
 // one 16-key half-block eight consecutive keys, the order the transposed V
