@@ -195,7 +195,8 @@ cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache,
  * k_cache, v_cache, block_table, ...), with T the plan's token count
  * ([DS] section 3.1: slot_mapping places every new token's K/V in the
  * cache; [CP] section 3.2.1: attention over cached and new keys).
- * Fusing the two is this library's design, not the pages'.
+ * Fusing the two is this library's own design; [DS] and [CP] run them as
+ * two steps.
  * The prefill kernel writes the new rows itself and reads every key at a
  * position >= H_s of its sequence from k_new / v_new instead of the cache,
  * so the write and the reads need no ordering and the separate write
