@@ -58,11 +58,6 @@ def features(chunk_lens, hist_lens) -> tuple[float, float, float]:
     return f0, f1, float(n)
 
 
-def model(a: float, b: float, c: float, C: float, H: float) -> float:
-    """f(C, H) for one sequence."""
-    return a * C * (C + H) + b * (C + H) + c
-
-
 def fit(feats, ms) -> tuple[float, float, float]:
     """Least squares (a, b, c) for ms ~ a*F0 + b*F1 + c*F2."""
     F = np.asarray(feats, dtype=np.float64).reshape(-1, 3)
