@@ -46,6 +46,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 HIST_SWEEP = (0, 4096, 8192, 12288)
 CHUNK = 512
+REPEATS = 3                      # event-free timed regions of the headline step
 
 
 def log(*a):
@@ -158,23 +159,11 @@ def headline(args):
         step()
         step_separate()
     torch.cuda.synchronize()
-    # Timed region: K steps exactly as a caller issues them. A recorded event
-    # costs 1.5-2 us of stream time (its own packet between two kernels), so
-    # none is recorded here.
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_separate()
-    torch.cuda.synchronize()
-    wall_sep = time.perf_counter() - t0
-    # Per-launch durations: the same K steps again with one event before the
-    # first call and one after every call, on the launch stream (torch's
-    # current stream); each call's time is the span between the events that
-    # bracket it, so it includes its launch and one event's overhead.
+    # Per-launch durations first (they also finish warming the clocks): K
+    # steps with one event before the first call and one after every call,
+    # on the launch stream (torch's current stream); each call's time is the
+    # span between the events that bracket it, so it includes its launch and
+    # one event's overhead.
     n = len(dbs)
     evs = [[Event() for _ in range(n + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -198,6 +187,25 @@ def headline(args):
             attention()
             e[2 * i + 2].record()
     torch.cuda.synchronize()
+    # Timed regions: K steps exactly as a caller issues them, with no event
+    # between the launches (a recorded event costs 1.5-2 us of stream time,
+    # its own packet between two kernels). The fused step is timed
+    # REPEATS times after the event passes; `value` is the first of these,
+    # and every repeat is reported.
+    walls = []
+    for _ in range(REPEATS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    wall = walls[0]
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_separate()
+    torch.cuda.synchronize()
+    wall_sep = time.perf_counter() - t0
     per_h = []
     call_ms_tot = 0.0
     for i, h in enumerate(args.hist):
@@ -216,8 +224,10 @@ def headline(args):
             f"kv_write {per_h[-1]['kv_write_us_mean']:.1f} us + attention "
             f"{per_h[-1]['attn_us_mean']:.1f} us")
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events ({wall_ev*1e6/args.steps:.1f} us "
-        f"with {n+1} events); separate calls {wall_sep*1e6/args.steps:.1f} us")
+    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events (repeats "
+        + ", ".join(f"{w * 1e6 / args.steps:.1f}" for w in walls)
+        + f"; {wall_ev*1e6/args.steps:.1f} us with {n+1} events); separate calls "
+        f"{wall_sep*1e6/args.steps:.1f} us")
     total_flops = sum(flops)
     achieved = (total_flops / n) / (call_ms_tot / n * 1e-3) / 1e12
     # The timed steps' outputs (bf16 bits), for the parity figure of the
@@ -226,6 +236,7 @@ def headline(args):
     return {
         "outputs": outs,
         "ms_per_step": ms_per_step,
+        "ms_per_step_repeats": [w * 1e3 / args.steps for w in walls],
         "ms_per_step_with_events": wall_ev * 1e3 / args.steps,
         "ms_per_step_separate_calls": wall_sep * 1e3 / args.steps,
         "value": total_flops / (ms_per_step * 1e-3) / 1e12,
@@ -741,27 +752,39 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
 
 
-def kernel_source_digest(path):
-    """sha256[:16] of a HIP source with its comments and whitespace removed:
-    it changes when the code does, not when only a comment does."""
+def kernel_source_digest(*paths):
+    """sha256[:16] of one or more C++/HIP sources, in order, with comments and
+    whitespace removed: it changes when the code does, not when only a
+    comment does."""
     import hashlib
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_src):
+# The sources that decide what the prefill launch reads and writes: the
+# kernel itself, the planner (tiles, splits, partial rows) and the shared
+# layouts.
+_CSRC = os.path.join(ROOT, "chunked_prefill_attention_slot_amd", "csrc")
+TRAFFIC_SOURCES = tuple(os.path.join(_CSRC, f) for f in
+                        ("prefill_attn.hip", "api.cpp", "cpa_internal.h"))
+
+
+def load_traffic(sources=TRAFFIC_SOURCES):
     """HBM bytes per launch of the prefill kernel from the committed counter
-    summary, or None if it was taken on different kernel code."""
+    summary, or None if it was taken on different code."""
     path = os.path.join(ROOT, "profiles", "prefill_attn_llama3_8b_c512_traffic.txt")
     try:
         fields = dict(l.split(":", 1) for l in open(path).read().splitlines() if ":" in l)
     except OSError:
         return None, "no counter summary"
-    sha = kernel_source_digest(kernel_src)
+    sha = kernel_source_digest(*sources)
     if fields.get("kernel_code_digest", "").strip() != sha:
         return None, "kernel changed since the counters were taken"
     return float(fields["hbm_bytes_per_launch"]), fields.get("note", "").strip()
@@ -811,8 +834,7 @@ def main():
         "ms_per_step_with_events": head["ms_per_step_with_events"],
         "ms_per_step_separate_calls": head["ms_per_step_separate_calls"],
     }
-    traffic, note = load_traffic(os.path.join(ROOT, "chunked_prefill_attention_slot_amd", "csrc",
-                                              "prefill_attn.hip"))
+    traffic, note = load_traffic()
     out["roofline"]["traffic"] = traffic
     out["roofline"]["traffic_note"] = note
     # Algorithmic bytes per launch averaged over the sweep: K and V of every

@@ -61,7 +61,8 @@ class cpa_layer_desc(ctypes.Structure):
 
 class cpa_plan_options(ctypes.Structure):
     _fields_ = [("target_items", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("prefill_split", ctypes.c_int32), ("decode_split_keys", ctypes.c_int32)]
+                ("prefill_split", ctypes.c_int32), ("decode_split_keys", ctypes.c_int32),
+                ("min_split_keys", ctypes.c_int32)]
 
 
 class cpa_plan_info(ctypes.Structure):

@@ -39,7 +39,12 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kDefaultCus = 256;
 constexpr int kNumXcds = 8;
-constexpr int kMinSplitKeys = 1024;
+// A split costs the combine launch that merges its pieces, measured at
+// about as much as two 64-key tiles of one item (at d = 64 and d = 128
+// alike: a lone item's tiles are bound by memory latency, not by the
+// products): a tile is split only when that shortens the longest item by
+// more.
+constexpr int kCombineTiles = 2;
 constexpr int kDefaultDecodeSplit = 512;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -109,6 +114,7 @@ struct cpa_plan_s {
   int32_t group = 1;             // Hq / Hkv
   int32_t decode_group = 0;      // heads per decode item, 0 if no decode kernel
   int32_t part_rows = 0, max_combine_rows = 0, max_combine_splits = 0;
+  int32_t part_bf16 = 0;         // split partials O/l in bf16 (else fp32)
   int64_t visible_pairs = 0;
   std::vector<cpa::WorkItem> prefill, decode;
   std::vector<cpa::CombineItem> combine;
@@ -255,6 +261,7 @@ cpa_status attention_impl(cpa_plan plan, const void* q, const void* k_cache, con
   a.out = out;
   a.out_f32 = d.out_dtype == CPA_DTYPE_F32;
   a.part_o = ws + plan->off_part_o;
+  a.part_bf16 = plan->part_bf16;
   a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
   a.zeros = reinterpret_cast<const uint16_t*>(ws);
   a.k_new = nullptr;
@@ -345,8 +352,10 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   cpa_plan_options opt{};
   if (options) opt = *options;
   if (opt.target_items < 0 || opt.num_cus < 0 || opt.prefill_split < 0 ||
-      opt.decode_split_keys < 0)
+      opt.decode_split_keys < 0 || opt.min_split_keys < 0)
     return cpa::fail(CPA_ERR_INVALID_ARG, "plan options must be >= 0");
+  if (opt.min_split_keys % cpa::kSplitAlign != 0)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "min_split_keys must be a multiple of 64");
 
   cpa_plan_s* p = new (std::nothrow) cpa_plan_s();
   if (!p) return cpa::fail(CPA_ERR_INVALID_ARG, "plan_create: out of host memory");
@@ -385,26 +394,34 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
 
   // Split long prefill key ranges when the tiles alone cannot give every
   // compute unit one work item (one 8-wave item fills a CU); the piece size
-  // is the smallest that keeps all items in a single round. Items are also
-  // split so none touches more than kPrefillPageCap block-table entries.
+  // is the smallest that keeps all items in a single round. All items then
+  // run at once, so the launch lasts about as long as its longest item: the
+  // split is kept only if it shortens that item by more tiles than the
+  // combine launch costs. Items are also split so none touches more than
+  // kPrefillPageCap block-table entries.
   const int cus = opt.num_cus > 0 ? opt.num_cus : cpa::kDefaultCus;
   const int target = opt.target_items > 0 ? opt.target_items : cus;
   const int64_t page_cap_keys =
       ((int64_t)(cpa::kPrefillPageCap - 1) * desc->page_size) / cpa::kSplitAlign * cpa::kSplitAlign;
   int64_t chunk_keys = page_cap_keys;
   if (opt.prefill_split == 0 && (int64_t)tiles.size() < target && !tiles.empty()) {
-    int64_t total_keys = 0;
-    for (const Tile& t : tiles) total_keys += t.kv_len;
+    int64_t total_keys = 0, longest = 0;
+    for (const Tile& t : tiles) {
+      total_keys += t.kv_len;
+      longest = std::max<int64_t>(longest, t.kv_len);
+    }
     int64_t c = (int64_t)cpa::round_up((size_t)((total_keys + target - 1) / target),
                                        cpa::kSplitAlign);
-    c = std::max<int64_t>(c, cpa::kMinSplitKeys);
+    c = std::max<int64_t>(c, std::max(opt.min_split_keys, cpa::kSplitAlign));
     auto count = [&](int64_t ck) {
       int64_t items = 0;
       for (const Tile& t : tiles) items += (t.kv_len + ck - 1) / ck;
       return items;
     };
     while (count(c) > target) c += cpa::kSplitAlign;
-    chunk_keys = std::min(chunk_keys, c);
+    const int64_t tiles_unsplit = (longest + cpa::kSplitAlign - 1) / cpa::kSplitAlign;
+    if (opt.min_split_keys > 0 || tiles_unsplit - c / cpa::kSplitAlign > cpa::kCombineTiles)
+      chunk_keys = std::min(chunk_keys, c);
   }
   for (const Tile& t : tiles) {
     int nsplit = (int)((t.kv_len + chunk_keys - 1) / chunk_keys);
@@ -435,8 +452,12 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   p->off_combine = off;
   off = cpa::round_up(off + p->combine.size() * sizeof(cpa::CombineItem), cpa::kAlign);
   p->off_part_o = off;
-  // Split partials O/l are kept in the output's precision.
-  const size_t part_elem = desc->out_dtype == CPA_DTYPE_F32 ? sizeof(float) : sizeof(uint16_t);
+  // Split partials O/l are kept in the output's precision: bf16 partials
+  // halve the bytes the split items write and the combine reads, which
+  // shortens every split call measurably (fp32 partials of bf16 outputs
+  // cost 8-12 us per Llama-3-8B chunk at H = 4096..12288).
+  p->part_bf16 = desc->out_dtype == CPA_DTYPE_BF16;
+  const size_t part_elem = p->part_bf16 ? sizeof(uint16_t) : sizeof(float);
   off = cpa::round_up(off + (size_t)p->part_rows * desc->head_dim * part_elem, cpa::kAlign);
   p->off_part_ml = off;
   off = cpa::round_up(off + (size_t)p->part_rows * 2 * sizeof(float), cpa::kAlign);

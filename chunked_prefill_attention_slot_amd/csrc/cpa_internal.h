@@ -14,8 +14,8 @@ namespace cpa {
 // read KV head `kvh`, over keys [kv0, kv1). Packed row r of the item is
 // query q0 + r / nheads, head head0 + r % nheads. If part >= 0 the item
 // writes partials at partial rows part + r instead of the output: O/l
-// (0 where l = 0) in the output's precision, and fp32 (max, sum). Read
-// with scalar loads (uniform).
+// (0 where l = 0) in the plan's partial precision (AttnArgs::part_bf16),
+// and fp32 (max, sum). Read with scalar loads (uniform).
 struct WorkItem {
   int32_t seq, kvh, head0, nheads;
   int32_t tok0, q0, nq, hist;
@@ -45,7 +45,8 @@ struct AttnArgs {
   float scale_log2e;        // scale * log2(e): scores go to exp2 directly
   void* out;                // [T, Hq, d] bf16 or fp32
   int32_t out_f32;
-  void* part_o;             // [rows, d] split partials O/l: bf16 if out is bf16, else fp32
+  void* part_o;             // [rows, d] split partials O/l: bf16 if part_bf16, else fp32
+  int32_t part_bf16;
   float* part_ml;           // [rows, 2] fp32: max (log2 units), sum
   const uint16_t* zeros;    // >= 16 zero bytes: source for keys past a range
   // Fused KV write (prefill kernel only): the step's new K/V rows, their

@@ -237,15 +237,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = o2;
       }
     } else {
-      // Partial of a split key range: O/l in the output's precision.
+      // Partial of a split key range: O/l in the plan's partial precision.
       const size_t prow = (size_t)it.part + g;
       const float inv = (ll > 0.f) ? 1.f / ll : 0.f;
-      if (a.out_f32) {
-        f32x4 o4 = {oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv};
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + prow * D + d) = o4;
-      } else {
+      if (a.part_bf16) {
         u32x2 o2 = {pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv)};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.part_o) + prow * D + d) = o2;
+      } else {
+        f32x4 o4 = {oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.part_o) + prow * D + d) = o4;
       }
       if (d == 0) {
         a.part_ml[prow * 2 + 0] = mm;
@@ -256,10 +256,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
 }
 
 // Log-sum-exp merge of the split partials of one tile: thread -> (packed
-// row r, 8 consecutive d). Split k holds O_k/l_k, max m_k and sum l_k;
-// O = sum_k 2^(m_k - m) l_k (O_k/l_k) / sum_k 2^(m_k - m) l_k, m = max_k m_k.
+// row r, 8 consecutive d). Split k holds O_k/l_k (bf16 if PB16, else fp32),
+// max m_k and sum l_k; O = sum_k 2^(m_k - m) l_k (O_k/l_k) /
+// sum_k 2^(m_k - m) l_k, m = max_k m_k. F32 selects the output's precision.
 // B splits are read per batch: 4 when no tile of the plan has more, else 8.
-template <int D, bool F32, int B>
+template <int D, bool F32, bool PB16, int B>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
                                                       AttnArgs a) {
   constexpr int D8 = D / 8;
@@ -283,16 +284,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
       const int k = min(k0 + j, it.nsplit - 1);
       const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
       mlk[j] = ml[prow];
-      if constexpr (F32) {
-        const f32x4* po = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) +
-                                                          prow * D + d);
-        ok0[j] = po[0];
-        ok1[j] = po[1];
-      } else {
+      if constexpr (PB16) {
         const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) +
                                                          prow * D + d);
         ok0[j] = f32x4{bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
         ok1[j] = f32x4{bf16_lo(b[2]), bf16_hi(b[2]), bf16_lo(b[3]), bf16_hi(b[3])};
+      } else {
+        const f32x4* po =
+            reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + prow * D + d);
+        ok0[j] = po[0];
+        ok1[j] = po[1];
       }
     }
     float bm = mm;
@@ -344,14 +345,23 @@ hipError_t launch_decode_d(const WorkItem* items, int n, const AttnArgs& a, int 
   return hipGetLastError();
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool PB16>
 hipError_t launch_combine_t(const CombineItem* items, dim3 grid, int max_splits,
                             const AttnArgs& a, hipStream_t s) {
   if (max_splits <= 4)
-    hipLaunchKernelGGL((combine_kernel<D, F32, 4>), grid, dim3(256), 0, s, items, a);
+    hipLaunchKernelGGL((combine_kernel<D, F32, PB16, 4>), grid, dim3(256), 0, s, items, a);
   else
-    hipLaunchKernelGGL((combine_kernel<D, F32, 8>), grid, dim3(256), 0, s, items, a);
+    hipLaunchKernelGGL((combine_kernel<D, F32, PB16, 8>), grid, dim3(256), 0, s, items, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_combine_d(const CombineItem* items, dim3 grid, int max_splits,
+                            const AttnArgs& a, hipStream_t s) {
+  if (a.out_f32 && a.part_bf16) return launch_combine_t<D, true, true>(items, grid, max_splits, a, s);
+  if (a.out_f32) return launch_combine_t<D, true, false>(items, grid, max_splits, a, s);
+  if (a.part_bf16) return launch_combine_t<D, false, true>(items, grid, max_splits, a, s);
+  return launch_combine_t<D, false, false>(items, grid, max_splits, a, s);
 }
 
 }  // namespace
@@ -369,10 +379,8 @@ hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows,
   if (num_items == 0) return hipSuccess;
   const int threads = max_rows * (head_dim / 8);
   const dim3 grid(num_items, (threads + 255) / 256);
-  if (head_dim == 128 && a.out_f32) return launch_combine_t<128, true>(items, grid, max_splits, a, stream);
-  if (head_dim == 128) return launch_combine_t<128, false>(items, grid, max_splits, a, stream);
-  if (head_dim == 64 && a.out_f32) return launch_combine_t<64, true>(items, grid, max_splits, a, stream);
-  if (head_dim == 64) return launch_combine_t<64, false>(items, grid, max_splits, a, stream);
+  if (head_dim == 128) return launch_combine_d<128>(items, grid, max_splits, a, stream);
+  if (head_dim == 64) return launch_combine_d<64>(items, grid, max_splits, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -715,8 +715,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
                                                      __float_as_uint(l_run), false, false);
     l_tot = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
   }
-  // A split item's partial is O/l in the output's precision (a row with no
-  // visible key in the range has l = 0 and stores zeros), with fp32 (m, l).
+  // A split item's partial is O/l in the plan's partial precision (a row
+  // with no visible key in the range has l = 0 and stores zeros), with fp32
+  // (m, l).
   const bool split = it.part >= 0;
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   auto store_rows = [&](auto ec) __attribute__((always_inline)) {
@@ -761,7 +762,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       }
     }
   };
-  if (a.out_f32)
+  if (split ? !a.part_bf16 : a.out_f32)
     store_rows(ic<4>{});
   else
     store_rows(ic<2>{});

@@ -117,11 +117,15 @@ typedef struct cpa_plan_s* cpa_plan;
 
 /* Tuning knobs; zero selects the default for a field. */
 typedef struct cpa_plan_options {
-  int32_t target_items;     /* work items to aim for (default 2 x CUs) */
+  int32_t target_items;     /* work items to aim for (default: one per CU) */
   int32_t num_cus;          /* compute units to plan for (default 256) */
   int32_t prefill_split;    /* force this many key splits per prefill
                                tile (default: chosen from the work) */
   int32_t decode_split_keys;/* keys per decode split (default 512) */
+  int32_t min_split_keys;   /* smallest prefill split piece in keys, a
+                               multiple of 64; nonzero also keeps splits
+                               that the planner's cost rule would drop
+                               (default 0: chosen from the work) */
 } cpa_plan_options;
 
 /*
@@ -150,7 +154,7 @@ typedef struct cpa_plan_info {
   int32_t num_prefill_items;   /* work items of the MFMA kernel */
   int32_t num_decode_items;    /* work items of the decode kernel */
   int32_t num_combine_items;   /* tiles whose key range was split */
-  int32_t num_partial_rows;    /* fp32 partial rows in the workspace */
+  int32_t num_partial_rows;    /* fp32 partial rows (O/l, max, sum) in the workspace */
   int64_t visible_pairs;       /* sum over rows and q heads of keys seen */
   size_t workspace_bytes;
 } cpa_plan_info;

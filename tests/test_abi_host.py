@@ -166,6 +166,36 @@ def test_plan_counts_and_pairs(cpa):
     assert p.info()["num_prefill_items"] == 64
 
 
+def test_plan_splits_short_ranges_only_when_it_pays(cpa):
+    """Tiles too few to fill the CUs are split into pieces as short as one
+    64-key tile, but only when that shortens the longest item by more than
+    the combine launch costs (two tiles)."""
+    d = desc(cpa)
+    # Llama-3-8B chunk at H = 0: 64 tiles of 64 + 64t keys; 128-key pieces
+    # (2 tiles, down from 8) give 8 * (1+1+2+2+3+3+4+4) = 160 items.
+    info = cpa.cpa_plan_create(d, [512], [512]).info()
+    assert info["num_prefill_items"] == 160
+    assert info["num_combine_items"] == 48          # every tile longer than 128 keys
+    assert info["num_partial_rows"] == 256 * 8 * (2 + 2 + 3 + 3 + 4 + 4)
+    tiny = desc(cpa, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+                num_blocks=4096, max_blocks_per_seq=2100)
+    # 128 and 192 keys: at most 3 tiles, splitting saves 2 or less -> no split
+    for n in (32, 128, 192):
+        info = cpa.cpa_plan_create(tiny, [n], [n]).info()
+        assert info["num_prefill_items"] == 4 and info["num_combine_items"] == 0, n
+    # 256 keys: 4 tiles -> 1 tile saves 3 -> split into 16 one-tile items
+    info = cpa.cpa_plan_create(tiny, [256], [256]).info()
+    assert info["num_prefill_items"] == 16 and info["num_combine_items"] == 4
+    # a forced floor keeps the split even where the rule would drop it
+    info = cpa.cpa_plan_create(tiny, [128], [128], {"min_split_keys": 64}).info()
+    assert info["num_prefill_items"] == 8 and info["num_combine_items"] == 4
+    # never more items than CUs from splitting alone
+    for n in (512, 1024, 1536, 2048):
+        assert cpa.cpa_plan_create(tiny, [n], [n]).info()["num_prefill_items"] <= 256
+    with pytest.raises(cpa.CpaError):
+        cpa.cpa_plan_create(tiny, [128], [128], {"min_split_keys": 100})
+
+
 def test_plan_page_cap_splits(cpa):
     """A tile whose key range spans more block-table entries than one
     prefill item stages in LDS (2047) is split even when splitting is

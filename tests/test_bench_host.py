@@ -31,6 +31,15 @@ def test_code_digest_ignores_comments_only(tmp_path):
     c.write_text("int f(int x) {\n  return x + 2;  // one\n}\n")
     assert bench.kernel_source_digest(a) == bench.kernel_source_digest(b)
     assert bench.kernel_source_digest(a) != bench.kernel_source_digest(c)
+    # several files: order and content both count
+    assert bench.kernel_source_digest(a, c) != bench.kernel_source_digest(c, a)
+    assert bench.kernel_source_digest(a, c) == bench.kernel_source_digest(b, c)
+
+
+def test_traffic_digest_covers_planner_and_layouts():
+    names = [os.path.basename(p) for p in bench.TRAFFIC_SOURCES]
+    assert names == ["prefill_attn.hip", "api.cpp", "cpa_internal.h"]
+    assert all(os.path.exists(p) for p in bench.TRAFFIC_SOURCES)
 
 
 def test_more_than_one_gpu_is_refused():

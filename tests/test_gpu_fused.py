@@ -42,11 +42,16 @@ CASES = {
     # decode rows only: no prefill items, the write kernel runs first
     "decode_only": dict(seed=24, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
                         query_lens=[1, 1, 1], seq_lens=[500, 33, 1000]),
-    # MHA with 40 heads: more new rows than the prefill threads take, the
-    # write kernel runs first
+    # MHA with 40 heads, tiles left unsplit: more new rows than the 80
+    # prefill items' threads take, the write kernel runs first
     "mha40_unfused": dict(seed=25, num_q_heads=40, num_kv_heads=40, head_dim=128,
                           page_size=128, query_lens=[512], seq_lens=[600],
-                          rows={0: [0, 5, 88, 300, 511]}),
+                          rows={0: [0, 5, 88, 300, 511]}, options={"prefill_split": 1}),
+    # the same batch with the planner's own splits: enough items to take
+    # the writes in the prefill kernel
+    "mha40_split": dict(seed=25, num_q_heads=40, num_kv_heads=40, head_dim=128,
+                        page_size=128, query_lens=[512], seq_lens=[600],
+                        rows={0: [0, 5, 88, 300, 511]}),
 }
 
 
@@ -55,6 +60,7 @@ def build(case):
     c = dict(case)
     c.pop("rows", None)
     c.pop("out_dtype", None)
+    c.pop("options", None)
     if "llama3_hist" in c:
         return llama3_8b_chunk(c["llama3_hist"])
     seed = c.pop("seed")
@@ -69,9 +75,10 @@ def test_fused_equals_separate(name):
     od = case.get("out_dtype", 0)
     print(f"[case] fused {name}: q_lens {list(b.query_lens)} seq_lens {list(b.seq_lens)}",
           flush=True)
-    sep = H.DeviceBatch(b, out_dtype=od)
+    opts = case.get("options")
+    sep = H.DeviceBatch(b, out_dtype=od, options=opts)
     sep.run()
-    fus = H.DeviceBatch(b, out_dtype=od)
+    fus = H.DeviceBatch(b, out_dtype=od, options=opts)
     fus.kv_write_attention()
     torch.cuda.synchronize()
     info = fus.plan.info()

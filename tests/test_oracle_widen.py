@@ -19,6 +19,9 @@ import torch
 
 from oracle.attention import widen_bf16
 
+# signalling NaN patterns raise numpy's "invalid value" flag when widened
+pytestmark = pytest.mark.filterwarnings("ignore:invalid value encountered in cast")
+
 ALL = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
 EXP = (ALL.astype(np.uint32) >> 7) & 0xFF
 FRAC = ALL.astype(np.uint32) & 0x7F
