@@ -30,7 +30,8 @@ CPA_DTYPE_F32 = 1
 EXPORTS = (
     "cpa_last_error", "cpa_version", "cpa_kv_write", "cpa_plan_create",
     "cpa_plan_destroy", "cpa_plan_get_info", "cpa_plan_upload",
-    "cpa_attention", "cpa_kv_write_attention", "cpa_validate_metadata",
+    "cpa_attention", "cpa_kv_write_attention", "cpa_kv_write_attention_static",
+    "cpa_validate_metadata",
     "cpa_predictor_profile_sizes",
     "cpa_predictor_fit", "cpa_predictor_target", "cpa_predictor_next_chunk",
     "cpa_calib_features", "cpa_calib_fit", "cpa_calib_target", "cpa_calib_next_chunk",
@@ -115,6 +116,7 @@ _sig("cpa_plan_upload", ctypes.c_int32, _P, _P, ctypes.c_size_t, _P)
 _sig("cpa_attention", ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P)
 _sig("cpa_kv_write_attention", ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
      ctypes.c_size_t, _P)
+_sig("cpa_kv_write_attention_static", ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P)
 _sig("cpa_validate_metadata", ctypes.c_int32, ctypes.POINTER(cpa_layer_desc), _I32P,
      ctypes.c_int32, _I32P, _I32P, _I32P, ctypes.c_int32)
 _sig("cpa_predictor_profile_sizes", ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -275,6 +277,18 @@ def cpa_kv_write_attention(plan: Plan, q, k_new, v_new, slot_mapping, k_cache, v
         _dev(slot_mapping, "slot_mapping", 4), _dev(k_cache, "k_cache", 2),
         _dev(v_cache, "v_cache", 2), _dev(block_table, "block_table", 4), _dev(out, "out"),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20    # CPA_STATIC_SCRATCH_BYTES
+
+
+def cpa_kv_write_attention_static(plan: Plan, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                  block_table, out, stream=None):
+    _check(_lib.cpa_kv_write_attention_static(
+        plan.handle, _dev(q, "q", 2), _dev(k_new, "k_new", 2), _dev(v_new, "v_new", 2),
+        _dev(slot_mapping, "slot_mapping", 4), _dev(k_cache, "k_cache", 2),
+        _dev(v_cache, "v_cache", 2), _dev(block_table, "block_table", 4), _dev(out, "out"),
         _stream(stream)))
 
 

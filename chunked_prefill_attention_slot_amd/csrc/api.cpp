@@ -313,6 +313,19 @@ cpa_status attention_impl(cpa_plan plan, const void* q, const void* k_cache, con
 
 }  // namespace
 
+namespace cpa {
+
+size_t plan_workspace_bytes(cpa_plan plan) { return plan ? plan->ws_bytes : 0; }
+
+bool workspace_holds(cpa_plan plan, const void* workspace) {
+  if (!plan) return false;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws_owner.find(workspace);
+  return it != g_ws_owner.end() && it->second == plan->id;
+}
+
+}  // namespace cpa
+
 extern "C" {
 
 const char* cpa_last_error(void) { return cpa::last_error().c_str(); }

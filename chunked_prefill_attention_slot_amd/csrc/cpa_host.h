@@ -10,6 +10,11 @@ namespace cpa {
 
 std::string& last_error();
 
+// Device workspace bytes `plan` needs (0 for a NULL plan).
+size_t plan_workspace_bytes(cpa_plan plan);
+// Whether `workspace` holds `plan`'s work lists (its last cpa_plan_upload).
+bool workspace_holds(cpa_plan plan, const void* workspace);
+
 inline cpa_status fail(cpa_status code, const std::string& msg) {
   last_error() = msg;
   return code;

@@ -222,6 +222,33 @@ cpa_status cpa_kv_write_attention(cpa_plan plan, const void* q, const void* k_ne
                                   hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * call and results as cpa_kv_write_attention, with no workspace argument:
+ * the plan's work lists and split partials live in a static device array of
+ * CPA_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends. The call allocates nothing; when the
+ * array on the current device does not hold this plan's work lists (the
+ * first call, or another plan's call came in between) it uploads them there
+ * first, as cpa_plan_upload does (an asynchronous host-to-device copy on
+ * `stream` from the plan's host image: keep the plan alive until `stream`
+ * has passed it).
+ *   Limit: a plan whose workspace_bytes exceeds CPA_STATIC_SCRATCH_BYTES is
+ *   refused with CPA_ERR_WORKSPACE before any GPU work.
+ *   Sharing: every call on one GPU uses that GPU's one array. Calls that
+ *   overlap on one GPU (other streams, other host threads, other plans)
+ *   race on it; the caller orders them. cpa_plan_upload / cpa_attention on
+ *   caller workspaces are unaffected.
+ *   Other arguments, layouts, ownership and errors as cpa_kv_write_attention.
+ */
+#define CPA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+cpa_status cpa_kv_write_attention_static(cpa_plan plan, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* slot_mapping,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* block_table, void* out,
+                                         hipStream_t stream);
+
+/*
  * Host-side bounds check of metadata before it is trusted on the device:
  * every slot_mapping entry is < 0 or < NB*P and no slot repeats; every
  * block_table entry a sequence can reach (j < ceil(seq_len/P)) is in
