@@ -1,32 +1,45 @@
 """Bench: paged chunked-prefill attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...] [--no-cpu]
 
 One step = one pass of the hot path over the headline workload: a
 Llama-3-8B attention layer (32 q / 8 kv heads, d=128, bf16, 128-token
 pages) taking one 512-token chunk at each prefix H in {0, 4096, 8192,
 12288} (the history sweep of the dynamic-chunking design's problem
 statement; 512-token chunks of the vLLM chunked-prefill article): for each
-H, the chunk's K/V are written into the paged cache through slot_mapping,
-then attention runs over prefix + chunk. Metadata planning and upload
-happen once per workload, outside the timed region (a plan serves every
-layer of a batch step). Inputs are resident in HBM before timing starts.
+H, one call writes the chunk's K/V into the paged cache through
+slot_mapping and runs attention over prefix + chunk. Metadata planning and
+upload happen once per workload, outside the timed region (a plan serves
+every layer of a batch step). Inputs are resident in HBM before timing.
 
 The printed JSON line (last line of stdout) carries:
-  value      -- algorithmic TFLOP/s of the whole step (KV writes included),
-                FLOP per chunk = 4*Hq*d*C*(H + C/2), over K steps timed
-                with no events between the launches;
-  roofline   -- the step's call (cpa_kv_write_attention: the prefill MFMA
-                kernel with the KV write inside, then the split combine)
-                against bf16 dense MFMA peak, averaged over the four H, its
-                duration from HIP events in a second pass of K steps;
-  decode     -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
-                40/40 heads): algorithmic K+V+Q+O bytes / time vs HBM peak;
-  cpu_baseline -- the fp64 oracle on a bounded sample of the H=12288 chunk.
---extras adds the mixed batch, the 70B-like long-context sweep, the
-chunk-size predictor runs, the token-budget step loop under four chunk
-rules and the chunk-size sweep around 512 as extra fields (--serving adds
-only the last two).
+  value        -- algorithmic TFLOP/s of the whole step, FLOP per chunk =
+                  4*Hq*d*C*(H + C/2), over K steps timed with no events
+                  between the launches, after the per-call event passes
+                  (three such timed regions; all are reported);
+  roofline     -- the step's call (prefill MFMA kernel with the KV write
+                  inside, then the split combine) against bf16 dense MFMA
+                  peak, averaged over the four H, durations from HIP events;
+and one object per further leg (all run by default; --legs selects):
+  small        -- the 4/4-head d=64 parity chunk (H=192, C=64);
+  decode       -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
+                  40/40 heads): algorithmic K+V+Q+O bytes / time vs HBM peak;
+  mixed_batch  -- the LLaMA-13B mixed batch (decode rows + two 512-token
+                  chunks): whole call, the chunks alone in TFLOP/s, and the
+                  two-micro-batch split on two streams;
+  long_context -- 70B-like layer, 16 chunks of 2048 from H=0 to 30720,
+                  TFLOP/s per chunk;
+  predictor    -- dynamic chunking at the 4/4-head d=64 shape: 64 profiled
+                  sizes, quadratic fit, T, the 32768-token walk at align 128
+                  and 16 with per-chunk ratios to T and to the model, and
+                  an online-calibrated walk;
+  chunk_schedule -- the token-budget step loop under fixed 512, progressive
+                  [2048, 1024, 512], predictor and calibrated chunk rules
+                  (a 16-request stream and one 32768-token prompt), and the
+                  cost of chunk sizes around 512;
+  cpu_baseline -- the fp64 oracle on host cores over the same workloads,
+                  with GPU/oracle ratios and element-wise parity against
+                  this run's GPU outputs.
 """
 from __future__ import annotations
 
@@ -250,6 +263,26 @@ def headline(args):
     }
 
 
+def small_leg(args):
+    """The small workload (4/4 heads, d=64, H=192 cached, C=64 new, 16-token
+    pages): the fused call's time. Far too small to load the GPU; it is the
+    parity case, timed for the record."""
+    import torch
+    from chunked_prefill_attention_slot_amd.inputs import small_parity
+    from chunked_prefill_attention_slot_amd.device import DeviceBatch
+    b = small_parity()
+    db = DeviceBatch(b)
+    r = median_ms(db.bound_fused(), 50, 10)
+    f = flops_chunk(4, 64, 64, 192)
+    torch.cuda.synchronize()
+    out = db.out.cpu().numpy().view(np.uint16).copy()
+    res = {"workload": "4/4 heads, d=64, page 16, H=192, C=64 (fused KV write + attention)",
+           "us_median": r["median_ms"] * 1e3, "us_mean": r["mean_ms"] * 1e3, "flop": f,
+           "tflops": f / (r["median_ms"] * 1e-3) / 1e12}
+    log(f"[bench] small: {res['us_median']:.1f} us per fused call")
+    return res, (b, out)
+
+
 def decode_rows(args, mixed):
     """LLaMA-13B decode rows alone: a plan over the 16 query_len-1 rows of
     the mixed batch (its prefill chunks get query_len 0)."""
@@ -278,11 +311,18 @@ def decode_rows(args, mixed):
     return res
 
 
-def mixed_extras(args, mixed):
+def mixed_leg(args, mixed):
+    """The LLaMA-13B mixed batch on one flattened axis (16 decode rows, then
+    two 512-token chunks at H = 2048 and 6144; 1040 tokens of a 2048-token
+    budget): (i) the whole mixed call, (ii) its prefill chunks alone ->
+    TFLOP/s, (iii) the two-micro-batch split (dual-stream article, section
+    3.1) on two streams. Decode rows alone are the decode leg."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     b, db = mixed
     r_all = median_ms(db.bound()[1], args.decode_reps, 3)
+    torch.cuda.synchronize()
+    out_all = db.out.cpu().numpy().view(np.uint16).copy()
     nd = 16
     ql = [0] * nd + [int(x) for x in b.query_lens[nd:]]
     plan = cpa.cpa_plan_create(db.desc, ql, b.seq_lens)
@@ -293,12 +333,14 @@ def mixed_extras(args, mixed):
                      args.decode_reps, 3)
     pf_flops = sum(flops_chunk(40, 128, int(c), int(n) - int(c))
                    for c, n in zip(b.query_lens[nd:], b.seq_lens[nd:]))
-    res = {"mixed_call_us": r_all["mean_ms"] * 1e3,
-           "prefill_only_us": r_pf["mean_ms"] * 1e3,
-           "prefill_only_tflops": pf_flops / (r_pf["mean_ms"] * 1e-3) / 1e12}
+    res = {"workload": "llama13b mixed batch: 16 decode rows + 2 chunks of 512 at H=2048, 6144",
+           "mixed_call_us": r_all["mean_ms"] * 1e3,
+           "prefill_only_us": r_pf["mean_ms"] * 1e3, "prefill_flop": pf_flops,
+           "prefill_only_tflops": pf_flops / (r_pf["mean_ms"] * 1e-3) / 1e12,
+           "prefill_only_mfma_frac":
+               pf_flops / (r_pf["mean_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     log(f"[bench] llama13b mixed call {res['mixed_call_us']:.1f} us; prefill chunks alone "
         f"{res['prefill_only_us']:.1f} us = {res['prefill_only_tflops']:.1f} TFLOP/s")
-    # Two micro-batches (dual-stream article, section 3.1) on two streams.
     from chunked_prefill_attention_slot_amd.device import MicroBatchPair
     for mode, name in ((cpa.CPA_SPLIT_BALANCED, "balanced"), (cpa.CPA_SPLIT_SIMPLE, "simple")):
         split = cpa.cpa_split_point(b.query_lens, mode, 0.5, 64)
@@ -310,12 +352,14 @@ def mixed_extras(args, mixed):
         res[f"micro_batches_{name}"] = {"split": list(split), "two_stream_us": r_mb["mean_ms"] * 1e3}
         log(f"[bench] llama13b micro-batches ({name}, split {split}): two streams "
             f"{r_mb['mean_ms'] * 1e3:.1f} us vs one call {res['mixed_call_us']:.1f} us")
-    return res
+    return res, out_all
 
 
 def long_context(args):
     """70B-like layer (64 q / 8 kv heads): one 32768-token prompt prefilled in
-    16 chunks of 2048; each chunk = KV write + attention."""
+    16 chunks of 2048; each chunk = one fused KV write + attention call,
+    FLOP counted as 4*heads*d*C*(H + C/2). Returns the result and the last
+    chunk's GPU output."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     from chunked_prefill_attention_slot_amd.inputs import make_batch
@@ -323,33 +367,27 @@ def long_context(args):
     b = make_batch(5, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=128,
                    query_lens=[32768], seq_lens=[32768])
     db = DeviceBatch(b)
+    run = chunk_runner(db, cpa, torch)
     rows = []
     tot_f, tot_ms = 0.0, 0.0
     for c in range(16):
         h = 2048 * c
-        plan = cpa.cpa_plan_create(db.desc, [2048], [h + 2048])
-        ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
-        cpa.cpa_plan_upload(plan, ws)
-        sl = slice(h, h + 2048)
-        kn, vn, sm = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl]
-        q, out = db.q[sl], db.out[sl]
-
-        kv_write = cpa.bind_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
-        attention = cpa.bind_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
-
-        def chunk():
-            kv_write()
-            attention()
-        r = median_ms(chunk, 10, 2)
+        r = median_ms(run(h, 2048), 10, 2)
         f = flops_chunk(64, 128, 2048, h)
         tot_f += f
         tot_ms += r["median_ms"]
         rows.append({"H": h, "us": r["median_ms"] * 1e3,
-                     "tflops": f / (r["median_ms"] * 1e-3) / 1e12})
-    res = {"chunks": rows, "total_ms": tot_ms, "tflops": tot_f / (tot_ms * 1e-3) / 1e12,
+                     "tflops": f / (r["median_ms"] * 1e-3) / 1e12,
+                     "mfma_frac": f / (r["median_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+    torch.cuda.synchronize()
+    last = db.out[30720:].cpu().numpy().view(np.uint16).copy()
+    res = {"workload": "70B-like layer 64/8 heads, d=128, page 128: 16 chunks of 2048, "
+                       "H = 0..30720, fused KV write + attention per chunk",
+           "chunks": rows, "total_ms": tot_ms, "tflops": tot_f / (tot_ms * 1e-3) / 1e12,
            "mfma_frac": tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-    log(f"[bench] 70b-like 16x2048: {tot_ms:.2f} ms total, {res['tflops']:.1f} TFLOP/s")
-    return res
+    log(f"[bench] 70b-like 16x2048: {tot_ms:.2f} ms total, {res['tflops']:.1f} TFLOP/s; last "
+        f"chunk {rows[-1]['tflops']:.0f} TFLOP/s")
+    return res, (b, last)
 
 
 PREDICTOR_SHAPES = {
@@ -361,21 +399,17 @@ PREDICTOR_SHAPES = {
 
 
 def chunk_runner(db, cpa, torch):
-    """runner(L, c) -> a closure doing KV write + attention of the chunk
-    [L, L + c) of db's single sequence."""
+    """runner(L, c) -> a closure doing the KV write + attention of the chunk
+    [L, L + c) of db's single sequence in one fused call
+    (cpa_kv_write_attention), the unit every chunk of a prefill pays."""
     def runner(L, c):
         plan = cpa.cpa_plan_create(db.desc, [c], [L + c])
         ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
         cpa.cpa_plan_upload(plan, ws)
         sl = slice(L, L + c)
-        kn, vn, sm, q, out = db.k_new[sl], db.v_new[sl], db.slot_mapping[sl], db.q[sl], db.out[sl]
-
-        kv_write = cpa.bind_kv_write(db.desc, kn, vn, sm, db.k_cache, db.v_cache)
-        attention = cpa.bind_attention(plan, q, db.k_cache, db.v_cache, db.block_table, out, ws)
-
-        def f():
-            kv_write()
-            attention()
+        f = cpa.bind_kv_write_attention(plan, db.q[sl], db.k_new[sl], db.v_new[sl],
+                                        db.slot_mapping[sl], db.k_cache, db.v_cache,
+                                        db.block_table, db.out[sl], ws)
         f.plan = plan
         return f
     return runner
@@ -391,13 +425,70 @@ def profile_fit(runner):
     return sizes, ms, cpa.cpa_predictor_fit(sizes, ms)
 
 
-def predictor_run(args, align=128, shape="tiny", prompt=32768):
-    """Startup profiling at 64 sizes (2048 down to 32, H=0) of KV write +
-    attention, least-squares fit, target T = f(2048) - f(0), then a prompt
-    prefilled with predicted chunks (one-variable model); then the same
-    prompt again with online calibration of the two-variable model f(C,H)
-    (refitted from each chunk's measured time once 5 are held; before that
-    the one-variable model sizes the chunks). Reports measured/T per chunk."""
+def _ratio_stats(r, ok=None):
+    r = np.asarray(r, dtype=np.float64)
+    out = {"min": float(r.min()), "max": float(r.max()), "mean": float(r.mean()),
+           "cv": float(r.std() / r.mean()) if r.mean() else None,
+           "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1))}
+    if ok is not None:
+        out["frac_within_10pct_not_alignment_limited"] = \
+            float(np.mean(np.abs(r[ok] - 1) <= 0.1)) if ok.any() else None
+    return out
+
+
+def predictor_walk(runner, fit, align, prompt, cfg_kw=None):
+    """Prefill `prompt` tokens with chunks from cpa_predictor_next_chunk under
+    the profiled fit; time each chunk (median of 11 fused calls) and compare
+    it with the target and with the model (dynamic-chunking design,
+    "runtime: dynamic prediction"). Per chunk: measured/T, the model's own
+    ratio [f(L+x) - f(L)]/T (below 0.9 = alignment-limited: the align-down
+    removed more than a tenth of the solved chunk), measured/model,
+    (measured - c)/T (the measured time beyond the fitted per-call constant
+    c, which f(L+x) - f(L) cancels), and measured/f(base)."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    a, b, c = fit
+    cfg = cpa.predictor_cfg(align=align, **(cfg_kw or {}))
+    T = cpa.cpa_predictor_target(cfg, a, b)
+    f_base = a * 2048.0 * 2048.0 + b * 2048.0 + c
+
+    def f(x):
+        return a * x * x + b * x + c
+    rows = []
+    L = 0
+    while L < prompt:
+        ch, x = cpa.cpa_predictor_next_chunk(cfg, a, b, T, L, prompt - L)
+        if ch <= 0:
+            break
+        m = median_ms(runner(L, ch), 11, 2)["median_ms"]
+        model = f(L + ch) - f(L)
+        rows.append((L, ch, x, m, model))
+        L += ch
+    Ls, ch, raw, ms, model = (np.array(v, dtype=np.float64) for v in zip(*rows))
+    model_over_T = model / T
+    ok = model_over_T >= 0.9
+    return {"align": align, "T_ms": T, "f_base_ms": f_base, "num_chunks": len(rows),
+            "degenerate_fit": not (a > 0),
+            "meas_over_T": _ratio_stats(ms / T, ok),
+            "meas_minus_c_over_T": _ratio_stats((ms - c) / T, ok),
+            # a degenerate fit (a <= 0) models some chunks at <= 0 ms
+            "meas_over_model": _ratio_stats(ms / model) if np.all(model > 0) else None,
+            "meas_over_f_base": _ratio_stats(ms / f_base, ok),
+            "alignment_limited_chunks": int((~ok).sum()),
+            "chunks": {"L": Ls.astype(int).tolist(), "chunk": ch.astype(int).tolist(),
+                       "raw_x": [round(v, 3) for v in raw],
+                       "ms": [round(v, 5) for v in ms],
+                       "model_over_T": [round(v, 4) for v in model_over_T]}}
+
+
+def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
+    """The dynamic-chunking workload: profile the fused KV write + attention
+    at 64 sizes (2048 down to 32, H = 0), fit f(l) = a l^2 + b l + c, set
+    T = f(2048) - f(0), then prefill a 32768-token prompt with predicted
+    chunks at each alignment quantum (128 as the workload states, 16 as the
+    side run). Then the same prompt again with online calibration of the
+    two-variable model f(C, H) (refitted from each chunk's measured time once
+    5 are held; before that the one-variable model sizes the chunks).
+    Returns the result and the GPU outputs of the align-128 walk."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     from chunked_prefill_attention_slot_amd.inputs import make_batch
@@ -405,83 +496,67 @@ def predictor_run(args, align=128, shape="tiny", prompt=32768):
     b = make_batch(3, query_lens=[prompt], seq_lens=[prompt], **PREDICTOR_SHAPES[shape])
     db = DeviceBatch(b)
     runner = chunk_runner(db, cpa, torch)
-
     sizes, ms, (a, bb, c) = profile_fit(runner)
-    cfg = cpa.predictor_cfg(align=align)
-    T = cpa.cpa_predictor_target(cfg, a, bb)
-    f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c   # modelled latency of a base chunk at H=0
-
-    def f_model(x):
-        return a * x * x + bb * x + c
-
-    def summary(chunks, key):
-        r = np.array([cch[key] for cch in chunks])
-        return {"min": float(r.min()), "max": float(r.max()), "mean": float(r.mean()),
-                "cv": float(r.std() / r.mean()),
-                "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1))}
-
-    chunks = []
-    L = 0
-    while L < prompt:
-        ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
-        if ch <= 0:
-            break
-        m = median_ms(runner(L, ch), 11, 2)["median_ms"]
-        model_ratio = (f_model(L + ch) - f_model(L)) / T
-        chunks.append({"L": L, "chunk": ch, "raw_x": x, "ms": m, "meas_over_T": m / T,
-                       "model_over_T": model_ratio, "meas_over_f_base": m / f_base,
-                       "alignment_limited": model_ratio < 0.9})
-        L += ch
-    r = np.array([cch["meas_over_T"] for cch in chunks])
-    ok = np.array([not cch["alignment_limited"] for cch in chunks])
+    prof = np.array(ms)
+    res = {"shape": shape, "prompt": prompt, "fit": {"a": a, "b": bb, "c": c},
+           "profile_ms": [round(v, 5) for v in ms], "profile_sizes": [int(v) for v in sizes],
+           # sizes run from 2048 down to 32: a rising profile has ms[i] >= ms[i+1]
+           "profile_monotone_violations": int(np.sum(prof[:-1] < prof[1:] - 1e-4)),
+           "fit_rms_ms": float(np.sqrt(np.mean((a * np.array(sizes, float) ** 2 +
+                                                bb * np.array(sizes, float) + c - prof) ** 2)))}
+    outputs = None
+    for al in aligns:
+        w = predictor_walk(runner, (a, bb, c), al, prompt)
+        res[f"align{al}"] = w
+        if outputs is None:
+            torch.cuda.synchronize()
+            outputs = (b, w["chunks"], db.out.cpu().numpy().view(np.uint16).copy())
+        log(f"[bench] predictor {shape} align {al}: a={a:.3e} b={bb:.3e} c={c:.3e} "
+            f"T={w['T_ms']:.4f} ms, {w['num_chunks']} chunks ({w['alignment_limited_chunks']} "
+            f"alignment-limited); meas/T mean {w['meas_over_T']['mean']:.2f} "
+            f"(within 10%: {w['meas_over_T']['frac_within_10pct']:.2f}); "
+            f"(meas-c)/T mean {w['meas_minus_c_over_T']['mean']:.2f} "
+            f"(within 10%: {w['meas_minus_c_over_T']['frac_within_10pct']:.2f}, not alignment-"
+            f"limited {w['meas_minus_c_over_T']['frac_within_10pct_not_alignment_limited']}); "
+            + (f"meas/model mean {w['meas_over_model']['mean']:.2f} cv "
+               f"{w['meas_over_model']['cv']:.2f}" if w["meas_over_model"] else
+               "model degenerate (a <= 0)"))
 
     # Online calibration of f(C, H) = a*C*(C+H) + b*(C+H) + c over the same prompt.
+    cfg = cpa.predictor_cfg(align=aligns[0])
+    T = cpa.cpa_predictor_target(cfg, a, bb)
+    f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c
     calib = cpa.Calib(min_points=5, window=30)
-    online = []
+    online, refused = [], 0
     L = 0
     while L < prompt:
         try:
             a2, b2, c2 = calib.model()
             T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
             ch, x = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
-            src = "online"
         except cpa.CpaError:
             ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
-            src = "profiled"
         if ch <= 0:
             break
         m = median_ms(runner(L, ch), 11, 2)["median_ms"]
         try:
             calib.record(cpa.cpa_calib_features([ch], [L]), m)
-            refit = True
         except cpa.CpaError:
-            refit = False   # window does not determine the model (e.g. one chunk size)
-        online.append({"L": L, "chunk": ch, "raw_x": x, "ms": m, "model": src, "refit": refit,
-                       "meas_over_f_base": m / f_base})
+            refused += 1       # window does not determine the model (e.g. one chunk size)
+        online.append((L, ch, m))
         L += ch
     try:
-        a2, b2, c2 = calib.model()
+        fin = list(calib.model())
     except cpa.CpaError:
-        a2 = b2 = c2 = None
-
-    res = {"shape": shape, "prompt": prompt, "align": align, "fit": {"a": a, "b": bb, "c": c},
-           "T_ms": T, "f_base_ms": f_base,
-           "profile_ms": dict(zip(map(int, sizes), ms)), "num_chunks": len(chunks),
-           "meas_over_T": summary(chunks, "meas_over_T"),
-           "frac_within_10pct": float(np.mean(np.abs(r - 1) <= 0.1)),
-           "frac_within_10pct_not_alignment_limited":
-               float(np.mean(np.abs(r[ok] - 1) <= 0.1)) if ok.any() else None,
-           "meas_over_f_base": summary(chunks, "meas_over_f_base"),
-           "chunks": chunks,
-           "online": {"num_chunks": len(online), "final_fit": {"a": a2, "b": b2, "c": c2},
-                      "refused_refits": sum(1 for o in online if not o["refit"]),
-                      "meas_over_f_base": summary(online, "meas_over_f_base"),
-                      "chunks": online}}
-    log(f"[bench] predictor {shape} align {align}: a={a:.3e} b={bb:.3e} c={c:.3e} T={T:.4f} ms, "
-        f"{len(chunks)} chunks, meas/T in [{r.min():.2f}, {r.max():.2f}]; online: "
-        f"{len(online)} chunks, meas/f(base) cv {res['online']['meas_over_f_base']['cv']:.3f} "
-        f"vs {res['meas_over_f_base']['cv']:.3f}")
-    return res
+        fin = None
+    om = np.array([m for _, _, m in online])
+    res["online"] = {"num_chunks": len(online), "final_fit": fin, "refused_refits": refused,
+                     "meas_over_f_base": _ratio_stats(om / f_base),
+                     "chunk": [int(ch) for _, ch, _ in online]}
+    log(f"[bench] predictor {shape} online calibration: {len(online)} chunks, meas/f(base) "
+        f"cv {res['online']['meas_over_f_base']['cv']:.3f} vs "
+        f"{res['align128']['meas_over_f_base']['cv']:.3f} profiled")
+    return res, outputs
 
 
 LLAMA3_8B = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128)
@@ -674,29 +749,66 @@ def alignment_study(args, hists=(0, 4096, 12288),
     return out
 
 
-def cpu_baseline(budget_s=10.0, gpu_outputs=None):
-    """The fp64 oracle on host cores over the headline step: the Llama-3-8B
-    chunk at H = 0, 4096, 8192, 12288, every query head, repeated until
-    budget_s seconds have passed (whole passes only). Its first pass is also
-    compared element by element with the outputs of the timed GPU steps
-    (gpu_outputs: H -> bf16 bits [512, 32, 128])."""
-    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
-    from oracle.attention import causal_chunk_attention, gather_sequence, widen_bf16
-    from oracle.kv_cache import kv_write
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
         blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
                 for i in threadpool_info()]
-        threads = max([i["threads"] or 1 for i in blas] or [1])
+        return blas, max([i["threads"] or 1 for i in blas] or [1])
     except Exception:
-        blas, threads = [], os.cpu_count()
+        return [], os.cpu_count()
+
+
+class _Parity:
+    """Running max / mean of |gpu - oracle| over compared elements."""
+
+    def __init__(self):
+        self.mx, self.tot, self.n = 0.0, 0.0, 0
+
+    def add(self, gpu_bits, ref):
+        g = (np.asarray(gpu_bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        e = np.abs(g - ref)
+        self.mx = max(self.mx, float(e.max()))
+        self.tot += float(e.sum())
+        self.n += e.size
+
+    def result(self):
+        return {"max_abs": self.mx, "mean_abs": self.tot / max(1, self.n), "elements": self.n,
+                "within_bar": self.mx <= 2e-2 and self.tot / max(1, self.n) <= 2e-3}
+
+
+def cpu_baseline(gpu, budget_s=8.0):
+    """The fp64 oracle on host cores, timed on the same workloads as the GPU
+    legs of this run, and compared element by element with their GPU
+    outputs (bar: max-abs 2e-2, mean-abs 2e-3):
+      * headline: whole passes of the Llama-3-8B step (C=512 at H = 0, 4096,
+        8192, 12288, all 32 query heads, including the page gather) until
+        budget_s has passed -- `value` is its FLOP rate;
+      * small: the 4/4-head d=64 chunk, in full;
+      * predictor: the chunk walk over the 32768-token prompt (the oracle's
+        schedule from the GPU fit's coefficients, checked equal to the
+        library's) and the attention of every chunk, in full;
+      * mixed: the LLaMA-13B mixed batch, every row, in full;
+      * long_context (subset): the last 2048-token chunk (H = 30720) for the
+        8 query heads of KV head 0, of the 64.
+    gpu: dict of the GPU legs' outputs and times."""
+    from chunked_prefill_attention_slot_amd.inputs import llama3_8b_chunk
+    from oracle.attention import (causal_chunk_attention, gather_sequence, paged_attention,
+                                  widen_bf16)
+    from oracle.kv_cache import kv_write
+    from oracle import predictor as opred
+    blas, threads = _blas_threads()
+    per = {}
+
+    # headline step (config 2)
     prepared = []
     for h in HIST_SWEEP:
         b = llama3_8b_chunk(h)
         kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
         prepared.append((h, b, kc, vc))
+    head_out = gpu.get("headline")
     passes = 0
-    parity = {}
+    par = {h: _Parity() for h in HIST_SWEEP}
     t0 = time.perf_counter()
     while True:
         for h, b, kc, vc in prepared:
@@ -707,36 +819,118 @@ def cpu_baseline(budget_s=10.0, gpu_outputs=None):
             for head in range(32):
                 o = causal_chunk_attention(q[:, head], k[:, head // 4], v[:, head // 4], h,
                                            1.0 / math.sqrt(128))
-                if passes == 0 and gpu_outputs is not None and h in gpu_outputs:
-                    g = (gpu_outputs[h][:, head].astype(np.uint32) << 16).view(np.float32)
-                    e = np.abs(g.astype(np.float64) - o)
-                    acc = parity.setdefault(h, [0.0, 0.0, 0])
-                    acc[0] = max(acc[0], float(e.max()))
-                    acc[1] += float(e.sum())
-                    acc[2] += e.size
+                if passes == 0 and head_out is not None and h in head_out["outputs"]:
+                    par[h].add(head_out["outputs"][h][:, head], o)
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     f = passes * sum(flops_chunk(32, 128, CHUNK, h) for h in HIST_SWEEP)
-    try:
-        aff = len(os.sched_getaffinity(0))
-    except Exception:
-        aff = os.cpu_count()
+    per["headline"] = {"seconds": dt, "passes": passes, "oracle_tflops": f / dt / 1e12,
+                       "oracle_ms_per_step": dt / passes * 1e3}
+    if head_out is not None:
+        per["headline"]["gpu_ms_per_step"] = head_out["ms_per_step"]
+        per["headline"]["gpu_over_oracle"] = dt / passes * 1e3 / head_out["ms_per_step"]
+        per["headline"]["parity_vs_gpu"] = {str(h): p.result() for h, p in par.items()}
     res = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{passes} pass(es) of the headline step (Llama-3-8B, C=512 at H=0/4096/"
                      f"8192/12288, all 32 query heads), fp64 NumPy oracle incl. gather; {dt:.1f} s",
-           "seconds": dt, "cpu_count": os.cpu_count(), "affinity": aff, "blas": blas}
-    if parity:
-        res["parity_vs_gpu"] = {
-            "note": "oracle vs the timed GPU steps' bf16 outputs, every element; bar: "
-                    "max-abs 2e-2, mean-abs 2e-3",
-            "per_H": {str(h): {"max_abs": m, "mean_abs": t / c} for h, (m, t, c) in parity.items()},
-            "max_abs": max(m for m, _, _ in parity.values()),
-            "mean_abs": sum(t for _, t, _ in parity.values()) / sum(c for _, _, c in parity.values())}
-        log(f"[bench] parity of the timed steps vs the oracle: max_abs "
-            f"{res['parity_vs_gpu']['max_abs']:.2e}, mean_abs {res['parity_vs_gpu']['mean_abs']:.2e}")
-    log(f"[bench] cpu oracle: {passes} passes in {dt:.1f} s -> {res['value']*1e3:.2f} GFLOP/s")
+           "seconds": dt, "cpu_count": os.cpu_count(), "blas": blas}
+    try:
+        res["affinity"] = len(os.sched_getaffinity(0))
+    except Exception:
+        res["affinity"] = os.cpu_count()
+
+    def timed(name, fn, gpu_ms, flop, note):
+        t = time.perf_counter()
+        p = fn()
+        d = time.perf_counter() - t
+        per[name] = {"seconds": d, "flop": flop, "oracle_tflops": flop / d / 1e12 if flop else None,
+                     "gpu_ms": gpu_ms, "gpu_over_oracle": d * 1e3 / gpu_ms if gpu_ms else None,
+                     "covers": note, "parity_vs_gpu": p.result() if p is not None else None}
+        log(f"[bench] cpu oracle {name}: {d:.2f} s"
+            + (f", GPU {d * 1e3 / gpu_ms:.0f}x faster" if gpu_ms else "")
+            + (f"; parity max_abs {p.mx:.2e} mean_abs {p.tot / max(1, p.n):.2e}" if p else ""))
+
+    if "small" in gpu:
+        b, out, us = gpu["small"]
+
+        def run_small():
+            p = _Parity()
+            kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+            p.add(out, paged_attention(b.q, kc, vc, b.block_table, b.query_lens, b.seq_lens,
+                                       b.num_kv_heads, b.page_size))
+            return p
+        timed("small", run_small, us * 1e-3, flops_chunk(4, 64, 64, 192), "every element")
+
+    if "predictor" in gpu:
+        b, chunks, out, fit, gpu_ms = gpu["predictor"]
+
+        def run_pred():
+            a, bb, c = fit
+            cfg = opred.PredictorConfig(align=128)
+            T = opred.target(a, bb, cfg.base_chunk_size)
+            sched = opred.schedule(cfg, a, bb, T, b.num_tokens)
+            per_chunks_equal = ([ch for _, ch, _ in sched] == chunks["chunk"] and
+                                [L for L, _, _ in sched] == chunks["L"])
+            p = _Parity()
+            kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+            n = b.num_tokens
+            k = widen_bf16(gather_sequence(kc, b.block_table[0], n, b.page_size))
+            v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size))
+            q = widen_bf16(b.q)
+            sc = 1.0 / math.sqrt(b.head_dim)
+            for L, ch, _ in sched:
+                for h in range(b.num_q_heads):
+                    g = h // (b.num_q_heads // b.num_kv_heads)
+                    o = causal_chunk_attention(q[L:L + ch, h], k[:L + ch, g], v[:L + ch, g], L, sc)
+                    p.add(out[L:L + ch, h], o)
+            per_chunks_ok.append(per_chunks_equal)
+            return p
+        per_chunks_ok = []
+        n = b.num_tokens
+        timed("predictor", run_pred, gpu_ms, 4.0 * b.num_q_heads * b.head_dim * n * n / 2.0,
+              "oracle schedule + attention of every chunk of the align-128 walk, every element")
+        per["predictor"]["schedule_equals_library"] = bool(per_chunks_ok[0])
+
+    if "mixed" in gpu:
+        b, out, us, pf_flops = gpu["mixed"]
+
+        def run_mixed():
+            p = _Parity()
+            kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+            p.add(out, paged_attention(b.q, kc, vc, b.block_table, b.query_lens, b.seq_lens,
+                                       b.num_kv_heads, b.page_size))
+            return p
+        timed("mixed", run_mixed, us * 1e-3, pf_flops,
+              "every row (16 decode rows, 2 prefill chunks); flop counts the chunks only")
+
+    if "long" in gpu:
+        b, last, us_last = gpu["long"]
+
+        def run_long():
+            p = _Parity()
+            kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+            n = b.num_tokens
+            k = widen_bf16(gather_sequence(kc, b.block_table[0], n, b.page_size)[:, 0])
+            v = widen_bf16(gather_sequence(vc, b.block_table[0], n, b.page_size)[:, 0])
+            q = widen_bf16(b.q[30720:, :8])
+            for h in range(8):
+                p.add(last[:, h], causal_chunk_attention(q[:, h], k, v, 30720,
+                                                         1.0 / math.sqrt(128)))
+            return p
+        # the GPU time of the same subset: the last chunk's call, 8 of its 64 heads
+        timed("long_context_subset", run_long, us_last * 1e-3 * 8 / 64,
+              flops_chunk(8, 128, 2048, 30720),
+              "last chunk (H=30720), query heads 0-7 of 64; GPU time prorated by heads")
+    res["per_config"] = per
+    bars = [v.get("parity_vs_gpu") for v in per.values()]
+    flat = [x for b_ in bars if b_ for x in (b_.values() if "max_abs" not in b_ else [b_])]
+    if flat:
+        res["parity_vs_gpu"] = {"max_abs": max(x["max_abs"] for x in flat),
+                                "all_within_bar": all(x["within_bar"] for x in flat)}
+    log(f"[bench] cpu oracle headline: {passes} passes in {dt:.1f} s -> {res['value']*1e3:.2f} "
+        f"GFLOP/s on {threads} threads")
     return res
 
 
@@ -790,22 +984,28 @@ def load_traffic(sources=TRAFFIC_SOURCES):
     return float(fields["hbm_bytes_per_launch"]), fields.get("note", "").strip()
 
 
+LEGS = ("headline", "small", "decode", "mixed", "long", "predictor", "schedule")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-reps", type=int, default=30)
-    ap.add_argument("--extras", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS) +
+                         " (the headline always runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--hist", type=int, nargs="+", default=list(HIST_SWEEP),
                     help="prefixes of the headline sweep (profiling subsets)")
-    ap.add_argument("--serving", action="store_true",
-                    help="add the step-loop and chunk-alignment legs (also part of --extras)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    legs = set(x for x in args.legs.split(",") if x)
+    unknown = legs - set(LEGS)
+    if unknown:
+        ap.error(f"unknown legs {sorted(unknown)}")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(each GPU would run its own heads or sequences with no exchange).",
@@ -818,6 +1018,7 @@ def main():
         return
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} CUs={props.multi_processor_count}")
+    t_start = time.perf_counter()
 
     head = headline(args)
     out = {
@@ -831,6 +1032,7 @@ def main():
                                "(cpa_kv_write_attention)",
                    "chunk": CHUNK, "hist": list(args.hist), "page_size": 128},
         "roofline": head["roofline"], "per_H": head["per_H"],
+        "ms_per_step_repeats": head["ms_per_step_repeats"],
         "ms_per_step_with_events": head["ms_per_step_with_events"],
         "ms_per_step_separate_calls": head["ms_per_step_separate_calls"],
     }
@@ -841,33 +1043,51 @@ def main():
     # visible key once, Q in, O out (bf16).
     alg = sum((h + CHUNK) * 8 * 128 * 2 * 2 + CHUNK * 32 * 128 * 2 * 2 for h in args.hist)
     out["roofline"]["algorithmic_bytes_per_launch"] = alg / len(args.hist)
-    if not args.no_decode or args.extras:
+    gpu = {"headline": {"outputs": head.pop("outputs"), "ms_per_step": head["ms_per_step"]}}
+    if "small" in legs:
+        out["small"], (b, o) = small_leg(args)
+        gpu["small"] = (b, o, out["small"]["us_median"])
+    if legs & {"decode", "mixed"}:
         from chunked_prefill_attention_slot_amd.inputs import mixed_llama13b
         from chunked_prefill_attention_slot_amd.device import DeviceBatch
         b = mixed_llama13b()
         mixed = (b, DeviceBatch(b))
         mixed[1].kv_write()
         torch.cuda.synchronize()
-        if not args.no_decode:
+        if "decode" in legs:
             out["decode"] = decode_rows(args, mixed)
-        if args.extras:
-            out["mixed_batch"] = mixed_extras(args, mixed)
+        if "mixed" in legs:
+            out["mixed_batch"], o = mixed_leg(args, mixed)
+            gpu["mixed"] = (b, o, out["mixed_batch"]["mixed_call_us"],
+                            out["mixed_batch"]["prefill_flop"])
         del mixed
         torch.cuda.empty_cache()
-    if args.extras:
-        out["long_context"] = long_context(args)
-        out["predictor"] = predictor_run(args, 128)
-        out["predictor_align16"] = predictor_run(args, 16)
-        out["predictor_llama3_8b"] = predictor_run(args, 128, shape="llama3_8b")
-    if args.extras or args.serving:
-        out["step_loop"] = serving_run(args)
-        out["alignment"] = alignment_study(args)
+    if "long" in legs:
+        out["long_context"], (b, last) = long_context(args)
+        gpu["long"] = (b, last, out["long_context"]["chunks"][-1]["us"])
+        torch.cuda.empty_cache()
+    if "predictor" in legs:
+        # the workload as stated (4/4 heads, d=64, 16-token pages) ...
+        out["predictor"], (b, chunks, o) = predictor_run(args)
+        fit = out["predictor"]["fit"]
+        gpu["predictor"] = (b, chunks, o, (fit["a"], fit["b"], fit["c"]),
+                            float(sum(chunks["ms"])))
+        torch.cuda.empty_cache()
+        # ... and the same procedure at the headline layer
+        out["predictor_llama3_8b"], _ = predictor_run(args, shape="llama3_8b", aligns=(128,))
+        torch.cuda.empty_cache()
+    if "schedule" in legs:
+        out["chunk_schedule"] = {"step_loop": serving_run(args),
+                                 "sizes_around_512": alignment_study(args)}
+        torch.cuda.empty_cache()
+    out["gpu_legs_seconds"] = time.perf_counter() - t_start
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(gpu_outputs=head.pop("outputs"))
+        out["cpu_baseline"] = cpu_baseline(gpu)
     out["context_from_pages"] = {
         "note": "whole-model figures on A100 from the vLLM chunked-prefill article, "
                 "section 2.1; not this kernel, not comparable",
         "llama13b_2048_token_prefill_ms": 120, "decode_ms_per_token": 25}
+    out["total_seconds"] = time.perf_counter() - t_start
     print(json.dumps(out), flush=True)
 
 
