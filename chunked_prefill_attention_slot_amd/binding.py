@@ -15,7 +15,10 @@ from typing import Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpa.so")
+# CPA_LIBRARY may name another build of the same ABI (the host sanitizer
+# build of tests/sanitize loads this way); by default the in-tree library.
+LIB_PATH = os.environ.get("CPA_LIBRARY") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpa.so")
 
 CPA_OK = 0
 CPA_ERR_INVALID_ARG = -1

@@ -130,34 +130,46 @@ struct Tile {
   int32_t seq, kvh, head0, nheads, tok0, q0, nq, hist, kv_len;
 };
 
-void add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, int nsplit,
+// Largest plan: work items (48 bytes each, on the host and in the
+// workspace) and partial rows (indexed in 32 bits by the kernels).
+constexpr int64_t kMaxPlanItems = (int64_t)1 << 21;
+constexpr int64_t kMaxPartialRows = ((int64_t)1 << 31) - 1;
+
+// Appends the items of tile t; false (nothing appended) if the plan would
+// outgrow kMaxPlanItems or kMaxPartialRows.
+bool add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, int64_t nsplit,
                int align) {
   cpa::WorkItem base{t.seq, t.kvh, t.head0, t.nheads, t.tok0, t.q0, t.nq, t.hist, 0, t.kv_len, -1, 0};
   // The key range is cut into `align`-key units dealt out as evenly as
   // possible (piece sizes differ by at most one unit), so split items of a
   // tile finish together.
-  const int units = (t.kv_len + align - 1) / align;
+  const int64_t units = ((int64_t)t.kv_len + align - 1) / align;
   nsplit = std::min(nsplit, units);
+  const int64_t items = (int64_t)p->prefill.size() + (int64_t)p->decode.size();
+  if (items + std::max<int64_t>(nsplit, 1) > kMaxPlanItems) return false;
   if (nsplit <= 1) {
     out.push_back(base);
-    return;
+    return true;
   }
   const int rows = t.nq * t.nheads;
+  if ((int64_t)p->part_rows + nsplit * rows > kMaxPartialRows) return false;
   const int part0 = p->part_rows;
-  p->part_rows += nsplit * rows;
+  p->part_rows += (int)(nsplit * rows);
   p->max_combine_rows = std::max(p->max_combine_rows, rows);
-  p->max_combine_splits = std::max(p->max_combine_splits, nsplit);
-  p->combine.push_back(cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, nsplit, part0, rows, 0});
-  int start = 0;
-  for (int k = 0; k < nsplit; ++k) {
-    const int n_units = units / nsplit + (k < units % nsplit ? 1 : 0);
+  p->max_combine_splits = std::max(p->max_combine_splits, (int)nsplit);
+  p->combine.push_back(
+      cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, (int)nsplit, part0, rows, 0});
+  int64_t start = 0;
+  for (int64_t k = 0; k < nsplit; ++k) {
+    const int64_t n_units = units / nsplit + (k < units % nsplit ? 1 : 0);
     cpa::WorkItem w = base;
-    w.kv0 = start * align;
-    w.kv1 = std::min(t.kv_len, (start + n_units) * align);
-    w.part = part0 + k * rows;
+    w.kv0 = (int32_t)(start * align);
+    w.kv1 = (int32_t)std::min<int64_t>(t.kv_len, (start + n_units) * align);
+    w.part = (int32_t)(part0 + k * rows);
     out.push_back(w);
     start += n_units;
   }
+  return true;
 }
 
 int64_t item_cost(const cpa::WorkItem& w) {
@@ -436,10 +448,11 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
     if (opt.min_split_keys > 0 || tiles_unsplit - c / cpa::kSplitAlign > cpa::kCombineTiles)
       chunk_keys = std::min(chunk_keys, c);
   }
+  bool fits = true;
   for (const Tile& t : tiles) {
-    int nsplit = (int)((t.kv_len + chunk_keys - 1) / chunk_keys);
-    if (opt.prefill_split > 0) nsplit = std::max(nsplit, opt.prefill_split);
-    add_split(p, p->prefill, t, nsplit, cpa::kSplitAlign);
+    int64_t nsplit = (t.kv_len + chunk_keys - 1) / chunk_keys;
+    if (opt.prefill_split > 0) nsplit = std::max<int64_t>(nsplit, opt.prefill_split);
+    fits = fits && add_split(p, p->prefill, t, nsplit, cpa::kSplitAlign);
   }
 
   const int dsk = opt.decode_split_keys > 0 ? opt.decode_split_keys : cpa::kDefaultDecodeSplit;
@@ -450,8 +463,15 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
     const int32_t n = seq_lens[s];
     for (int g = 0; g < Hkv; ++g) {
       Tile t{s, g, g * G, G, t0, 0, 1, n - 1, n};
-      add_split(p, p->decode, t, (n + dsk - 1) / dsk, 1);
+      fits = fits && add_split(p, p->decode, t, ((int64_t)n + dsk - 1) / dsk, 1);
     }
+  }
+  if (!fits) {
+    delete p;
+    return cpa::fail(CPA_ERR_UNSUPPORTED,
+                     "plan too large: more than " + std::to_string(kMaxPlanItems) +
+                         " work items or 2^31 partial rows (raise decode_split_keys or lower "
+                         "prefill_split)");
   }
   order_for_xcds(p->prefill, cpa::kNumXcds);
   order_for_xcds(p->decode, cpa::kNumXcds);

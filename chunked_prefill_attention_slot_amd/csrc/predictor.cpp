@@ -153,6 +153,11 @@ extern "C" cpa_status cpa_predictor_profile_sizes(int64_t base, int32_t n, int64
                                                   int64_t* sizes) {
   if (!sizes || n < 2 || lo < 1 || base <= lo)
     return cpa::fail(CPA_ERR_INVALID_ARG, "profile_sizes: need n >= 2, base > lo >= 1");
+  // n distinct sizes need a spacing of at least one token (with a spacing of
+  // exactly one every size is an integer, so the rounding merges none)
+  if (base - lo < (int64_t)n - 1)
+    return cpa::fail(CPA_ERR_INVALID_ARG, "profile_sizes: base - lo < n - 1 cannot give n "
+                                          "distinct sizes");
   for (int32_t i = 0; i < n; ++i) {
     const double v = (double)base - (double)i * (double)(base - lo) / (double)(n - 1);
     sizes[i] = (int64_t)std::nearbyint(v);

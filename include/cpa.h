@@ -140,6 +140,9 @@ typedef struct cpa_plan_options {
  * power of two in 16..1024, total tokens < 2^31.
  *   options may be NULL. *workspace_bytes receives the device workspace
  *   size cpa_attention needs. On error *out_plan is NULL.
+ * A plan of more than 2^21 work items or 2^31 - 1 split-partial rows (tiny
+ * decode_split_keys over long rows, huge prefill_split) is refused with
+ * CPA_ERR_UNSUPPORTED.
  */
 cpa_status cpa_plan_create(const cpa_layer_desc* desc,
                            const int32_t* query_lens, const int32_t* seq_lens,
@@ -283,7 +286,9 @@ typedef struct cpa_predictor_cfg {
 
 /*
  * [CPP] "startup: profiling": n distinct sizes spread evenly from base down
- * to lo: sizes[i] = round(base - i*(base-lo)/(n-1)). n >= 2, base > lo >= 1.
+ * to lo: sizes[i] = round(base - i*(base-lo)/(n-1)) (round half to even).
+ * Needs n >= 2, base > lo >= 1 and base - lo >= n - 1 (else the sizes could
+ * not all differ): CPA_ERR_INVALID_ARG otherwise.
  */
 cpa_status cpa_predictor_profile_sizes(int64_t base, int32_t n, int64_t lo,
                                        int64_t* sizes);

@@ -44,6 +44,18 @@ def test_profile_sizes_match_oracle(cpa):
         assert cpa.cpa_predictor_profile_sizes(base, n, lo) == profile_sizes(base, n, lo)
 
 
+def test_profile_sizes_distinct_or_refused(cpa):
+    """n sizes from base down to lo are distinct exactly when base - lo >=
+    n - 1; fewer tokens than that are refused rather than repeated."""
+    s = cpa.cpa_predictor_profile_sizes(100, 65, 36)      # spacing exactly 1
+    assert s == list(range(100, 35, -1))
+    s = cpa.cpa_predictor_profile_sizes(101, 41, 20)      # spacing 2.025
+    assert len(set(s)) == 41 and s[0] == 101 and s[-1] == 20
+    for base, n, lo in ((100, 66, 36), (40, 64, 32), (2048, 2, 2048)):
+        with pytest.raises(cpa.CpaError):
+            cpa.cpa_predictor_profile_sizes(base, n, lo)
+
+
 def test_target_bit_exact(cpa):
     from oracle.predictor import target
     cfg = cpa.predictor_cfg()
@@ -194,6 +206,18 @@ def test_plan_splits_short_ranges_only_when_it_pays(cpa):
         assert cpa.cpa_plan_create(tiny, [n], [n]).info()["num_prefill_items"] <= 256
     with pytest.raises(cpa.CpaError):
         cpa.cpa_plan_create(tiny, [128], [128], {"min_split_keys": 100})
+
+
+def test_plan_refuses_oversized_plans(cpa):
+    """Decode rows split into one-key ranges would need billions of work
+    items and partial rows: refused, not wrapped around in 32 bits."""
+    d = desc(cpa, num_q_heads=40, num_kv_heads=40, num_blocks=40000, max_blocks_per_seq=256)
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_plan_create(d, [1] * 64, [32768] * 64, {"decode_split_keys": 1})
+    assert e.value.status == cpa.CPA_ERR_UNSUPPORTED and "too large" in cpa.cpa_last_error()
+    # the same batch with the default split is fine
+    assert cpa.cpa_plan_create(d, [1] * 64, [32768] * 64).info()["num_decode_items"] == \
+        64 * 40 * 64
 
 
 def test_plan_page_cap_splits(cpa):
