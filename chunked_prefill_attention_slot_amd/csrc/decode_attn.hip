@@ -321,14 +321,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
   const float inv = 1.f / ll;
   const int qi = r / it.nheads, hl = r - qi * it.nheads;
   const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D + d;
+  // Streaming stores: nothing in this launch reads the rows again.
   if constexpr (F32) {
     f32x4* po = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob);
-    po[0] = o0 * inv;
-    po[1] = o1 * inv;
+    __builtin_nontemporal_store(o0 * inv, po);
+    __builtin_nontemporal_store(o1 * inv, po + 1);
   } else {
     const u32x4 o = {pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
                      pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob));
   }
 }
 

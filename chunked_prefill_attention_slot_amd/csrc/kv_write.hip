@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
       (((page * num_kv_heads + h) << page_log2) + off) * chunks_per_row + c;
   const u32x4 kv = __builtin_nontemporal_load(&k_new[idx]);
   const u32x4 vv = __builtin_nontemporal_load(&v_new[idx]);
-  k_cache[dst] = kv;
-  v_cache[dst] = vv;
+  __builtin_nontemporal_store(kv, &k_cache[dst]);
+  __builtin_nontemporal_store(vv, &v_cache[dst]);
 }
 
 }  // namespace

@@ -252,8 +252,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         const uint32_t h = rem / CPT, c = rem % CPT;
         const int64_t page = slot >> a.page_log2, off = slot & ((1 << a.page_log2) - 1);
         const int64_t dst = (((page * a.num_kv_heads + h) << a.page_log2) + off) * CPT + c;
-        reinterpret_cast<u32x4*>(a.k_cache_w)[dst] = kw_k[k];
-        reinterpret_cast<u32x4*>(a.v_cache_w)[dst] = kw_v[k];
+        __builtin_nontemporal_store(kw_k[k], reinterpret_cast<u32x4*>(a.k_cache_w) + dst);
+        __builtin_nontemporal_store(kw_v[k], reinterpret_cast<u32x4*>(a.v_cache_w) + dst);
       }
     }
   }
