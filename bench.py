@@ -16,7 +16,8 @@ The printed JSON line (last line of stdout) carries:
   value        -- algorithmic TFLOP/s of the whole step, FLOP per chunk =
                   4*Hq*d*C*(H + C/2), over K steps timed with no events
                   between the launches, after the per-call event passes
-                  (three such timed regions; all are reported);
+                  (the median of three such timed regions; all are
+                  reported);
   roofline     -- the step's call (prefill MFMA kernel with the KV write
                   inside, then the split combine) against bf16 dense MFMA
                   peak, averaged over the four H, durations from HIP events;
@@ -203,8 +204,9 @@ def headline(args):
     # Timed regions: K steps exactly as a caller issues them, with no event
     # between the launches (a recorded event costs 1.5-2 us of stream time,
     # its own packet between two kernels). The fused step is timed
-    # REPEATS times after the event passes; `value` is the first of these,
-    # and every repeat is reported.
+    # REPEATS times after the event passes, each region exactly K steps;
+    # `value` is the median region (the clock still settles over the first
+    # regions after a short warm-up), and every repeat is reported.
     walls = []
     for _ in range(REPEATS):
         torch.cuda.synchronize()
@@ -213,7 +215,7 @@ def headline(args):
             step()
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
-    wall = walls[0]
+    wall = sorted(walls)[len(walls) // 2]
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step_separate()
@@ -237,7 +239,7 @@ def headline(args):
             f"kv_write {per_h[-1]['kv_write_us_mean']:.1f} us + attention "
             f"{per_h[-1]['attn_us_mean']:.1f} us")
     ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events (repeats "
+    log(f"[bench] step: {ms_per_step*1e3:.1f} us without events (median of repeats "
         + ", ".join(f"{w * 1e6 / args.steps:.1f}" for w in walls)
         + f"; {wall_ev*1e6/args.steps:.1f} us with {n+1} events); separate calls "
         f"{wall_sep*1e6/args.steps:.1f} us")
