@@ -20,7 +20,8 @@ The printed JSON line (last line of stdout) carries:
                   reported);
   roofline     -- the step's call (prefill MFMA kernel with the KV write
                   inside, then the split combine) against bf16 dense MFMA
-                  peak, averaged over the four H, durations from HIP events;
+                  peak, averaged over the four H; a call's duration is the
+                  span of K back-to-back calls between two HIP events, / K;
 and one object per further leg (all run by default; --legs selects):
   small        -- the 4/4-head d=64 parity chunk (H=192, C=64);
   decode       -- LLaMA-13B decode rows (16 rows, seq_len U[1024, 8192],
@@ -173,10 +174,10 @@ def headline(args):
         step()
         step_separate()
     torch.cuda.synchronize()
-    # Per-launch durations first (they also finish warming the clocks): K
-    # steps with one event before the first call and one after every call,
-    # on the launch stream (torch's current stream); each call's time is the
-    # span between the events that bracket it, so it includes its launch and
+    # Event passes first (they also finish warming the clocks): K steps with
+    # one event before the first call and one after every call, on the
+    # launch stream (torch's current stream); each call's bracketed time is
+    # the span between the events around it, so it includes its launch and
     # one event's overhead.
     n = len(dbs)
     evs = [[Event() for _ in range(n + 1)] for _ in range(args.steps)]
@@ -200,6 +201,22 @@ def headline(args):
             e[2 * i + 1].record()
             attention()
             e[2 * i + 2].record()
+    torch.cuda.synchronize()
+    # Per-call durations without per-call event overhead: for each H, K
+    # back-to-back calls of that chunk between one pair of events on the
+    # launch stream; the duration of a call is the span over K. This is the
+    # figure `per_H` and `roofline` use; the bracketed spans above (each call
+    # between two events of its own) are kept beside it.
+    per_call = []
+    for f in fused:
+        e0, e1 = Event(), Event()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        e1.synchronize()
+        per_call.append(e0.elapsed_time(e1) / args.steps)
     torch.cuda.synchronize()
     # Timed regions: K steps exactly as a caller issues them, with no event
     # between the launches (a recorded event costs 1.5-2 us of stream time,
@@ -227,17 +244,20 @@ def headline(args):
         c = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
         a = sorted(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for e in evs_sep)
         kv = sorted(e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs_sep)
-        cm = sum(c) / len(c)
+        cm = per_call[i]
         call_ms_tot += cm
-        per_h.append({"H": h, "call_us_mean": cm * 1e3, "call_us_median": c[len(c) // 2] * 1e3,
+        per_h.append({"H": h, "call_us_mean": cm * 1e3,
+                      "call_us_bracketed_mean": sum(c) / len(c) * 1e3,
+                      "call_us_bracketed_median": c[len(c) // 2] * 1e3,
                       "attn_us_mean": sum(a) / len(a) * 1e3,
                       "kv_write_us_mean": sum(kv) / len(kv) * 1e3,
                       "tflops": flops[i] / (cm * 1e-3) / 1e12,
                       "mfma_frac": flops[i] / (cm * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
         log(f"[bench] H={h}: kv_write_attention {cm*1e3:.1f} us -> {per_h[-1]['tflops']:.1f} "
-            f"TFLOP/s ({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak); separate calls: "
+            f"TFLOP/s ({100*per_h[-1]['mfma_frac']:.1f}% of bf16 peak; {sum(c) / len(c) * 1e3:.1f}"
+            f" us between events of its own); separate calls: "
             f"kv_write {per_h[-1]['kv_write_us_mean']:.1f} us + attention "
-            f"{per_h[-1]['attn_us_mean']:.1f} us")
+            f"{per_h[-1]['attn_us_mean']:.1f} us (events of their own)")
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] step: {ms_per_step*1e3:.1f} us without events (median of repeats "
         + ", ".join(f"{w * 1e6 / args.steps:.1f}" for w in walls)
@@ -260,7 +280,9 @@ def headline(args):
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None,
                      "kernel": "cpa_kv_write_attention (prefill_kernel<128, fused> + "
-                               "combine_kernel<128>)",
+                               "combine_kernel<128> when tiles are split)",
+                     "duration": "mean call duration, K back-to-back calls per H between "
+                                 "two HIP events on the launch stream, averaged over the H",
                      "flop_per_launch": total_flops / n},
     }
 
