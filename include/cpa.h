@@ -157,7 +157,8 @@ typedef struct cpa_plan_info {
   int32_t num_prefill_items;   /* work items of the MFMA kernel */
   int32_t num_decode_items;    /* work items of the decode kernel */
   int32_t num_combine_items;   /* tiles whose key range was split */
-  int32_t num_partial_rows;    /* fp32 partial rows (O/l, max, sum) in the workspace */
+  int32_t num_partial_rows;    /* split-partial rows in the workspace: O/l in the
+                                  output's precision, fp32 max and sum */
   int64_t visible_pairs;       /* sum over rows and q heads of keys seen */
   size_t workspace_bytes;
 } cpa_plan_info;
@@ -188,7 +189,10 @@ cpa_status cpa_plan_upload(cpa_plan plan, void* workspace,
  *   block_table: device [num_seqs, max_blocks_per_seq] int32.
  *   out: device [T, Hq, d], bf16 or fp32 per desc->out_dtype.
  *   workspace: the buffer passed to cpa_plan_upload for this plan.
- * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax.
+ * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax. Rows
+ * whose keys were split over several work items are merged by a second
+ * kernel from partials kept in the output's precision (bf16 or fp32), with
+ * fp32 max and sum.
  */
 cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_table,
