@@ -249,6 +249,8 @@ def headline(args):
         per_h.append({"H": h, "call_us_mean": cm * 1e3,
                       "call_us_bracketed_mean": sum(c) / len(c) * 1e3,
                       "call_us_bracketed_median": c[len(c) // 2] * 1e3,
+                      "call_us_bracketed_p10": c[len(c) // 10] * 1e3,
+                      "call_us_bracketed_p90": c[(9 * len(c)) // 10] * 1e3,
                       "attn_us_mean": sum(a) / len(a) * 1e3,
                       "kv_write_us_mean": sum(kv) / len(kv) * 1e3,
                       "tflops": flops[i] / (cm * 1e-3) / 1e12,
