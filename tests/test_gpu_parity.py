@@ -287,3 +287,39 @@ def test_long_context_chunk2048(H, hist):
     from chunked_prefill_attention_slot_amd.inputs import long_context_chunk
     b = long_context_chunk(hist)
     run_and_compare(H, b, f"70b-like C2048 H{hist}", rows={0: sample_rows(2048, 12, hist)})
+
+
+@pytest.mark.parametrize("shape", [
+    dict(num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=16),     # decode kernel, G = 1
+    dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128),   # decode kernel, G = 4
+    dict(num_q_heads=32, num_kv_heads=2, head_dim=64, page_size=32),     # G = 16: MFMA kernel
+])
+def test_decode_row_equals_last_prefill_row(H, shape):
+    """The last row of a prefill chunk and a decode row (query_len 1) over
+    the same sequence see the same keys with the same query: the two paths
+    (for G <= 8 two different kernels) agree within the tolerance, and each
+    matches the oracle."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from chunked_prefill_attention_slot_amd.inputs import make_batch
+    n, C = 3000, 200
+    b = make_batch(61, query_lens=[C], seq_lens=[n], extra_pages=2, **shape)
+    print(f"[case] decode row vs last prefill row {shape}", flush=True)
+    db = H.DeviceBatch(b)
+    db.run()                                  # KV write then prefill attention
+    plan = cpa.cpa_plan_create(db.desc, [1], [n])
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    cpa.cpa_plan_upload(plan, ws)
+    q1 = db.q[C - 1:C].contiguous()
+    out1 = torch.full_like(db.out[:1], -7777)
+    cpa.cpa_attention(plan, q1, db.k_cache, db.v_cache, db.block_table, out1, ws)
+    torch.cuda.synchronize()
+    widen = lambda t: (t.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    pre, dec = widen(db.out[C - 1]), widen(out1[0])
+    err = np.abs(pre.astype(np.float64) - dec)
+    print(f"[parity] decode row vs prefill row: max_abs={err.max():.3e}", flush=True)
+    assert err.max() <= H.MAX_ABS
+    ref = H.oracle_out(b, rows={0: [C - 1]})
+    H.compare(db.out_f64(), ref, "prefill last row")
+    got = np.full_like(ref, np.nan)
+    got[C - 1] = dec
+    H.compare(got, ref, "decode row")
