@@ -506,6 +506,19 @@ def predictor_walk(runner, fit, align, prompt, cfg_kw=None):
                        "model_over_T": [round(v, 4) for v in model_over_T]}}
 
 
+def seed_calibration(calib, sizes, ms):
+    """Start the online calibration's record window with the startup
+    profile's timed runs (dynamic-chunking design, "startup: profiling" and
+    "online calibration"): each is a chunk of l tokens at H = 0, i.e. the
+    features [l*l, l, 1], added in ascending size so that the sizes nearest
+    the base stay longest in the window. Without them, a single prompt whose
+    profile model repeats one chunk size never gets a refit: C*(C+H) and
+    C+H then stay proportional and the window does not determine a, b, c."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    for l, m in sorted(zip(sizes, ms)):
+        calib.record(cpa.cpa_calib_features([int(l)], [0]), float(m))
+
+
 def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
     """The dynamic-chunking workload: profile the fused KV write + attention
     at 64 sizes (2048 down to 32, H = 0), fit f(l) = a l^2 + b l + c, set
@@ -513,7 +526,9 @@ def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
     chunks at each alignment quantum (128 as the workload states, 16 as the
     side run). Then the same prompt again with online calibration of the
     two-variable model f(C, H) (refitted from each chunk's measured time once
-    5 are held; before that the one-variable model sizes the chunks).
+    5 are held), twice: with the record window seeded by the startup
+    profile's timed runs (seed_calibration), and unseeded (the one-variable
+    model sizes the chunks until a refit exists).
     Returns the result and the GPU outputs of the align-128 walk."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
@@ -552,43 +567,54 @@ def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
     cfg = cpa.predictor_cfg(align=aligns[0])
     T = cpa.cpa_predictor_target(cfg, a, bb)
     f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c
-    calib = cpa.Calib(min_points=5, window=30)
-    online, refused = [], 0
-    L = 0
-    while L < prompt:
+    for key, seeded in (("online", True), ("online_unseeded", False)):
+        calib = cpa.Calib(min_points=5, window=30)
+        if seeded:
+            seed_calibration(calib, sizes, ms)
+        online, refused = [], 0
+        L = 0
+        while L < prompt:
+            try:
+                a2, b2, c2 = calib.model()
+                T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
+                ch, x = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
+            except cpa.CpaError:
+                T2 = f_base
+                ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
+            if ch <= 0:
+                break
+            m = median_ms(runner(L, ch), 11, 2)["median_ms"]
+            try:
+                calib.record(cpa.cpa_calib_features([ch], [L]), m)
+            except cpa.CpaError:
+                refused += 1       # window does not determine the model (e.g. one chunk size)
+            online.append((L, ch, m, T2))
+            L += ch
         try:
-            a2, b2, c2 = calib.model()
-            T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
-            ch, x = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
+            fin = list(calib.model())
         except cpa.CpaError:
-            ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
-        if ch <= 0:
-            break
-        m = median_ms(runner(L, ch), 11, 2)["median_ms"]
-        try:
-            calib.record(cpa.cpa_calib_features([ch], [L]), m)
-        except cpa.CpaError:
-            refused += 1       # window does not determine the model (e.g. one chunk size)
-        online.append((L, ch, m))
-        L += ch
-    try:
-        fin = list(calib.model())
-    except cpa.CpaError:
-        fin = None
-    om = np.array([m for _, _, m in online])
-    res["online"] = {"num_chunks": len(online), "final_fit": fin, "refused_refits": refused,
-                     "meas_over_f_base": _ratio_stats(om / f_base),
-                     "chunk": [int(ch) for _, ch, _ in online]}
-    log(f"[bench] predictor {shape} online calibration: {len(online)} chunks, meas/f(base) "
-        f"cv {res['online']['meas_over_f_base']['cv']:.3f} vs "
-        f"{res['align128']['meas_over_f_base']['cv']:.3f} profiled")
+            fin = None
+        om = np.array([r[2] for r in online])
+        res[key] = {"seeded_with_profile": seeded, "num_chunks": len(online), "final_fit": fin,
+                    "refused_refits": refused,
+                    # T' of the model that sized each chunk (f(base) of the profile fit
+                    # while no refit exists)
+                    "meas_over_T_used": _ratio_stats(om / np.array([r[3] for r in online])),
+                    "meas_over_f_base": _ratio_stats(om / f_base),
+                    "chunk": [int(r[1]) for r in online]}
+        log(f"[bench] predictor {shape} online calibration ({'seeded' if seeded else 'unseeded'}): "
+            f"{len(online)} chunks, {refused} refits refused; meas/T' mean "
+            f"{res[key]['meas_over_T_used']['mean']:.2f} cv {res[key]['meas_over_T_used']['cv']:.3f} "
+            f"(within 10%: {res[key]['meas_over_T_used']['frac_within_10pct']:.2f}); meas/f(base) "
+            f"cv {res[key]['meas_over_f_base']['cv']:.3f} vs "
+            f"{res['align128']['meas_over_f_base']['cv']:.3f} profiled")
     return res, outputs
 
 
 LLAMA3_8B = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128)
 
 
-def step_loop(requests, budget, rule, fit, seed=7, align=128):
+def step_loop(requests, budget, rule, fit, seed=7, align=128, profile=None):
     """One pass of the token-budget step loop (vLLM chunked-prefill article,
     section 3.1) over a request stream at the Llama-3-8B layer: libcpa's
     batch former forms each step, the stream lays out its metadata, and the
@@ -597,7 +623,9 @@ def step_loop(requests, budget, rule, fit, seed=7, align=128):
     host waits for the step (so host work is outside the figure). rule is
     ("fixed", size) | ("progressive", sizes) | ("predictor",) |
     ("calibrated",): the last refits f(C, H) online from every step's
-    features and time and hands the model to the former."""
+    features and time, its window seeded with the startup profile's runs
+    (profile = (sizes, ms); seed_calibration), and hands the model to the
+    former."""
     import torch
     from chunked_prefill_attention_slot_amd import binding as cpa
     from chunked_prefill_attention_slot_amd.device import ServingCaches
@@ -619,6 +647,10 @@ def step_loop(requests, budget, rule, fit, seed=7, align=128):
     for p, m, t in requests:
         sched.add(p, m, t)
     calib = cpa.Calib(min_points=5, window=30) if kind == "calibrated" else None
+    if calib is not None and profile is not None:
+        seed_calibration(calib, *profile)
+        a2, b2, c2 = calib.model()
+        sched.set_model(a2, b2, c2, cpa.cpa_calib_target(pcfg, a2, b2, c2))
     stream = ServingStream(seed, requests=requests, **LLAMA3_8B)
     dev = ServingCaches(stream, init="zeros")
     g = torch.Generator(device="cuda")
@@ -736,7 +768,7 @@ def serving_run(args):
     for name, reqs in (("stream16", llama3_8b_request_stream()), ("single32k", [(32768, 0, 0)])):
         rows = []
         for rule in rules:
-            r = step_loop(reqs, 2048, rule, fit)
+            r = step_loop(reqs, 2048, rule, fit, profile=(sizes, ms))
             rows.append(r)
             bs = r["step_ms_with_prefill"]
             log(f"[bench] step loop {name} {r['rule']}: {r['steps']} steps, {r['gpu_ms_total']:.1f} "

@@ -281,6 +281,52 @@ def test_calib_features_match_oracle(cpa):
         assert cpa.cpa_calib_features(C, H) == features(C, H)
 
 
+def test_calib_one_chunk_size_is_refused_unless_seeded(cpa):
+    """Records of a single prompt whose chunks all have one size C leave
+    C*(C+H) and C+H proportional: every refit is refused and no model ever
+    exists. A window seeded with the startup profile's runs (H = 0, sizes
+    2048 .. 32) takes the same records and keeps a model."""
+    import bench
+    from oracle.predictor import profile_sizes
+    recs = [(cpa.cpa_calib_features([1280], [1280 * i]), 0.015 + 1e-6 * i) for i in range(12)]
+    bare = cpa.Calib(min_points=5, window=30)
+    for i, (f, m) in enumerate(recs):
+        if i < 4:
+            assert bare.record(f, m) is False        # fewer than min_points: no fit yet
+        else:
+            with pytest.raises(cpa.CpaError):
+                bare.record(f, m)
+    with pytest.raises(cpa.CpaError):
+        bare.model()
+    sizes = profile_sizes(2048, 64, 32)
+    seeded = cpa.Calib(min_points=5, window=30)
+    bench.seed_calibration(seeded, sizes, [1e-9 * l * l + 2e-6 * l + 0.012 for l in sizes])
+    for f, m in recs:
+        assert seeded.record(f, m) is True
+    seeded.model()
+
+
+def test_calib_seeded_with_profile_is_the_profile_quadratic(cpa):
+    """At H = 0 the two-variable model is the one-variable quadratic
+    (features [l*l, l, 1]), so a window seeded with the profile holds the 30
+    largest sizes and fits the same coefficients as the one-variable least
+    squares over them: the library's fit and the oracle's."""
+    import bench
+    from oracle.predictor import fit_quadratic, profile_sizes
+    sizes = profile_sizes(2048, 64, 32)
+    rng = np.random.default_rng(11)
+    ms = [2e-8 * l * l + 3e-6 * l + 0.012 + float(rng.normal(0, 2e-4)) for l in sizes]
+    calib = cpa.Calib(min_points=5, window=30)
+    bench.seed_calibration(calib, sizes, ms)
+    got = calib.model()
+    top = sorted(zip(sizes, ms))[-30:]
+    assert top[0][0] == 1120 and top[-1][0] == 2048
+    tl, tm = [l for l, _ in top], [m for _, m in top]
+    for exp in (fit_quadratic(tl, tm), cpa.cpa_predictor_fit(tl, tm)):
+        for g, e in zip(got, exp):
+            assert abs(g - e) <= 1e-7 * abs(e), (got, exp)
+
+
 def test_calib_fit_matches_oracle(cpa):
     from oracle.calibration import features, fit
     rng = np.random.default_rng(8)
