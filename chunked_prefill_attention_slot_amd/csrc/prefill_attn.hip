@@ -175,6 +175,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int qi = r / it.nheads;
   const int hl = r - qi * it.nheads;
   const bool row_ok = qi < it.nq;
+  // A wave whose 32 packed rows all lie past the item's rows (a chunk
+  // shorter than the item) keeps only its share of the tile copies, the
+  // waits and the barriers, and leaves its SIMD to the partner wave. At
+  // d = 128 the test held across the loop costs scalar-register spills
+  // (16 -> 23) and slowed full items, so only the d = 64 kernel takes it.
+  const bool busy = D != 64 || 32 * w < it.nq * it.nheads;
   const int qpos = it.hist + it.q0 + qi;
 
   // Q is copied into LDS first (buffers 2 and 3, which the first tile
@@ -644,8 +650,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       // group 1 runs X(0). Both then copy their share of tile 2.
       wait_tile(0);
       __syncthreads();
-      x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
-      if constexpr (G == 0) y_phase(0);
+      if (busy) x_phase(0, ic<0>{}, std::false_type{}, std::true_type{});
+      if constexpr (G == 0) {
+        if (busy) y_phase(0);
+      }
       if (2 < ntiles) issue(it.kv0 + 2 * BN, pg2, 2, ic<3>{});
       // Steady half steps h = 2 .. 2n-1: X(s) with 1 <= s <= n-1, Y(s) with
       // s <= n-1 for either group, buffers known at compile time from h % 8.
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
         constexpr int SJ = ((J - G + 8) % 8) >> 1;  // s % 4
         const int s = (h - G) >> 1;
         if constexpr (X) {
-          x_phase(((SJ + 3) % 4) * TILE, ic<SJ>{}, std::true_type{}, std::true_type{});
+          if (busy) x_phase(((SJ + 3) % 4) * TILE, ic<SJ>{}, std::true_type{}, std::true_type{});
         } else {
           constexpr int AH = 2 + G;                  // tile copied in this Y phase
           const int tc = s + AH;
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
           const bool copy = tc < ntiles;
           const int pg = __builtin_amdgcn_readfirstlane(pg_next);
           pg_next = page_raw(it.kv0 + (tc + 1) * BN);
-          y_phase(s);
+          if (busy) y_phase(s);
           if (copy) issue(it.kv0 + tc * BN, pg, (SJ + AH) % 4, ic<3>{});
         }
       };
@@ -694,8 +702,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
       // group 1 runs Y(n-1) then X(n).
       const int vlast = ((ntiles - 1) & 3) * TILE;
       __syncthreads();
-      if constexpr (G == 1) y_phase(ntiles - 1);
-      x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
+      if constexpr (G == 1) {
+        if (busy) y_phase(ntiles - 1);
+      }
+      if (busy) x_phase(vlast, ic<0>{}, std::true_type{}, std::false_type{});
     };
     if (grp == 0)
       run(ic<0>{});
