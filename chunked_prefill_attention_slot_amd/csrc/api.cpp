@@ -113,7 +113,12 @@ struct cpa_plan_s {
   int32_t num_seqs = 0, num_tokens = 0;
   int32_t group = 1;             // Hq / Hkv
   int32_t decode_group = 0;      // heads per decode item, 0 if no decode kernel
-  int32_t part_rows = 0, max_combine_rows = 0, max_combine_splits = 0;
+  int32_t part_rows = 0;
+  // Combine items of split prefill tiles come first, then those of split
+  // decode rows; each group has its own launch, sized by its own largest
+  // row count and split count (a decode tile has G rows, a prefill tile up
+  // to 256, and one grid for both would be mostly empty blocks).
+  int32_t combine_count[2] = {0, 0}, combine_rows[2] = {0, 0}, combine_splits[2] = {0, 0};
   int32_t part_bf16 = 0;         // split partials O/l in bf16 (else fp32)
   int64_t visible_pairs = 0;
   std::vector<cpa::WorkItem> prefill, decode;
@@ -155,8 +160,10 @@ bool add_split(cpa_plan_s* p, std::vector<cpa::WorkItem>& out, const Tile& t, in
   if ((int64_t)p->part_rows + nsplit * rows > kMaxPartialRows) return false;
   const int part0 = p->part_rows;
   p->part_rows += (int)(nsplit * rows);
-  p->max_combine_rows = std::max(p->max_combine_rows, rows);
-  p->max_combine_splits = std::max(p->max_combine_splits, (int)nsplit);
+  const int grp = (&out == &p->decode) ? 1 : 0;
+  p->combine_count[grp] += 1;
+  p->combine_rows[grp] = std::max(p->combine_rows[grp], rows);
+  p->combine_splits[grp] = std::max(p->combine_splits[grp], (int)nsplit);
   p->combine.push_back(
       cpa::CombineItem{t.tok0, t.head0, t.nheads, t.nq, (int)nsplit, part0, rows, 0});
   int64_t start = 0;
@@ -316,10 +323,12 @@ cpa_status attention_impl(cpa_plan plan, const void* q, const void* k_cache, con
   e = cpa::launch_decode(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_decode),
                          (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
   if (e != hipSuccess) return cpa::hip_fail(e, "decode attention launch");
-  e = cpa::launch_combine(reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine),
-                          (int)plan->combine.size(), plan->max_combine_rows,
-                          plan->max_combine_splits, a, d.head_dim, stream);
-  if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
+  const cpa::CombineItem* citems = reinterpret_cast<const cpa::CombineItem*>(ws + plan->off_combine);
+  for (int g = 0; g < 2; ++g) {
+    e = cpa::launch_combine(citems + (g ? plan->combine_count[0] : 0), plan->combine_count[g],
+                            plan->combine_rows[g], plan->combine_splits[g], a, d.head_dim, stream);
+    if (e != hipSuccess) return cpa::hip_fail(e, "split combine launch");
+  }
   return cpa::ok();
 }
 

@@ -255,33 +255,28 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
   }
 }
 
-// Log-sum-exp merge of the split partials of one tile: thread -> (packed
-// row r, 8 consecutive d). Split k holds O_k/l_k (bf16 if PB16, else fp32),
-// max m_k and sum l_k; O = sum_k 2^(m_k - m) l_k (O_k/l_k) /
-// sum_k 2^(m_k - m) l_k, m = max_k m_k. F32 selects the output's precision.
-// B splits are read per batch: 4 when no tile of the plan has more, else 8.
-template <int D, bool F32, bool PB16, int B>
-__global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
-                                                      AttnArgs a) {
-  constexpr int D8 = D / 8;
-  const CombineItem it = items[blockIdx.x];
-  const int idx = blockIdx.y * 256 + threadIdx.x;
-  const int r = idx / D8, d = 8 * (idx % D8);
-  if (r >= it.rows) return;
-  // Every load of a batch is issued before any is used (indices past the
-  // last split repeat it and get weight 0), so a batch costs one round trip
-  // to memory; earlier batches are rescaled to the running max. A split's
-  // (max, sum) pair is one 8-byte load, its 8 values one 16-byte load
-  // (bf16) or two (fp32).
+// Log-sum-exp merge of the split partials of one tile. Split k holds
+// O_k/l_k (bf16 if PB16, else fp32), max m_k and sum l_k; O = sum_k
+// 2^(m_k - m) l_k (O_k/l_k) / sum_k 2^(m_k - m) l_k, m = max_k m_k.
+//
+// fold_splits adds splits [k0, k1) of tile `it`, for packed row r and the 8
+// values from d, to a running (mm, ll, o0, o1): ll = sum 2^(m_k - mm) l_k
+// and o the same sum of weighted O_k. B splits are read per batch, every
+// load of a batch issued before any is used (indices past k1 - 1 repeat it
+// and get weight 0), so a batch costs one round trip to memory; earlier
+// batches are rescaled to the running max. A split's (max, sum) pair is one
+// 8-byte load, its 8 values one 16-byte load (bf16) or two (fp32).
+template <int D, bool PB16, int B>
+__device__ __forceinline__ void fold_splits(const CombineItem& it, const AttnArgs& a, int r, int d,
+                                            int k0, int k1, float& mm, float& ll, f32x4& o0,
+                                            f32x4& o1) {
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-  float mm = -INFINITY, ll = 0.f;
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
-  for (int k0 = 0; k0 < it.nsplit; k0 += B) {
+  for (int kb = k0; kb < k1; kb += B) {
     float2 mlk[B];
     f32x4 ok0[B], ok1[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int k = min(k0 + j, it.nsplit - 1);
+      const int k = min(kb + j, k1 - 1);
       const size_t prow = (size_t)it.part0 + (size_t)k * it.rows + r;
       mlk[j] = ml[prow];
       if constexpr (PB16) {
@@ -299,7 +294,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
     float bm = mm;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      if (k0 + j >= it.nsplit) mlk[j].x = -INFINITY;
+      if (kb + j >= k1) mlk[j].x = -INFINITY;
       bm = fmaxf(bm, mlk[j].x);
     }
     const float a0 = (mm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm - bm);
@@ -318,10 +313,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
     }
     mm = bm;
   }
+}
+
+// O = o / ll into the output row of packed row r (values d .. d+7). F32
+// selects the output's precision. Streaming stores: nothing in this launch
+// reads the rows again.
+template <int D, bool F32>
+__device__ __forceinline__ void store_merged(const CombineItem& it, const AttnArgs& a, int r, int d,
+                                             float ll, f32x4 o0, f32x4 o1) {
   const float inv = 1.f / ll;
   const int qi = r / it.nheads, hl = r - qi * it.nheads;
   const size_t ob = ((size_t)(it.tok0 + qi) * a.num_q_heads + it.head0 + hl) * D + d;
-  // Streaming stores: nothing in this launch reads the rows again.
   if constexpr (F32) {
     f32x4* po = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob);
     __builtin_nontemporal_store(o0 * inv, po);
@@ -331,6 +333,70 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restr
                      pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob));
   }
+}
+
+// Tiles with at most B splits (B = 4 or 8): thread -> (packed row r, 8
+// consecutive values), all splits in one batch.
+template <int D, bool F32, bool PB16, int B>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineItem* __restrict__ items,
+                                                      AttnArgs a) {
+  constexpr int D8 = D / 8;
+  const CombineItem it = items[blockIdx.x];
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  const int r = idx / D8, d = 8 * (idx % D8);
+  if (r >= it.rows) return;
+  float mm = -INFINITY, ll = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  fold_splits<D, PB16, B>(it, a, r, d, 0, it.nsplit, mm, ll, o0, o1);
+  store_merged<D, F32>(it, a, r, d, ll, o0, o1);
+}
+
+// Tiles with more than 8 splits (short chunks over long prefixes, long
+// decode rows): S threads share each (packed row, 8 values), each folding
+// one contiguous range of the splits, and their (m, l, O) meet in LDS,
+// where the first of them merges and stores. S = 2, 4 or 8 for up to 16,
+// 32 or more splits, so a group folds one batch of 8 up to 64 splits; one
+// thread walking all the splits would pay one memory round trip per batch
+// in sequence, and more groups than batches only multiply the blocks.
+template <int D, int S>
+constexpr int wide_rows_per_block() { return 256 / S / (D / 8); }
+
+template <int D, bool F32, bool PB16, int S>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const CombineItem* __restrict__ items,
+                                                           AttnArgs a) {
+  constexpr int D8 = D / 8, GT = 256 / S, RPB = wide_rows_per_block<D, S>();
+  static_assert(GT % D8 == 0 && RPB >= 1, "combine_wide_kernel thread layout");
+  __shared__ float s_m[256], s_l[256];
+  __shared__ f32x4 s_o0[256], s_o1[256];
+  const CombineItem it = items[blockIdx.x];
+  const int t = threadIdx.x, g = t / GT, lt = t % GT;
+  const int r = blockIdx.y * RPB + lt / D8, d = 8 * (lt % D8);
+  const bool valid = r < it.rows;
+  const int per = (it.nsplit + S - 1) / S;
+  const int k0 = min(g * per, it.nsplit), k1 = min(k0 + per, it.nsplit);
+  float mm = -INFINITY, ll = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  if (valid && k0 < k1) fold_splits<D, PB16, 8>(it, a, r, d, k0, k1, mm, ll, o0, o1);
+  s_m[t] = mm;
+  s_l[t] = ll;
+  s_o0[t] = o0;
+  s_o1[t] = o1;
+  __syncthreads();
+  if (g != 0 || !valid) return;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < S; ++j) m = fmaxf(m, s_m[j * GT + lt]);
+  float l = 0.f;
+  f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const float mj = s_m[j * GT + lt];
+    const float wj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - m);
+    l += wj * s_l[j * GT + lt];
+    p0 += wj * s_o0[j * GT + lt];
+    p1 += wj * s_o1[j * GT + lt];
+  }
+  store_merged<D, F32>(it, a, r, d, l, p0, p1);
 }
 
 template <int D>
@@ -347,8 +413,19 @@ hipError_t launch_decode_d(const WorkItem* items, int n, const AttnArgs& a, int 
 }
 
 template <int D, bool F32, bool PB16>
-hipError_t launch_combine_t(const CombineItem* items, dim3 grid, int max_splits,
+hipError_t launch_combine_t(const CombineItem* items, int num_items, int max_rows, int max_splits,
                             const AttnArgs& a, hipStream_t s) {
+  auto wide = [&](auto sc) {
+    constexpr int S = decltype(sc)::value, RPB = wide_rows_per_block<D, S>();
+    const dim3 grid(num_items, (max_rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((combine_wide_kernel<D, F32, PB16, S>), grid, dim3(256), 0, s, items, a);
+    return hipGetLastError();
+  };
+  if (max_splits > 32) return wide(std::integral_constant<int, 8>{});
+  if (max_splits > 16) return wide(std::integral_constant<int, 4>{});
+  if (max_splits > 8) return wide(std::integral_constant<int, 2>{});
+  const int threads = max_rows * (D / 8);
+  const dim3 grid(num_items, (threads + 255) / 256);
   if (max_splits <= 4)
     hipLaunchKernelGGL((combine_kernel<D, F32, PB16, 4>), grid, dim3(256), 0, s, items, a);
   else
@@ -357,12 +434,12 @@ hipError_t launch_combine_t(const CombineItem* items, dim3 grid, int max_splits,
 }
 
 template <int D>
-hipError_t launch_combine_d(const CombineItem* items, dim3 grid, int max_splits,
+hipError_t launch_combine_d(const CombineItem* items, int n, int max_rows, int max_splits,
                             const AttnArgs& a, hipStream_t s) {
-  if (a.out_f32 && a.part_bf16) return launch_combine_t<D, true, true>(items, grid, max_splits, a, s);
-  if (a.out_f32) return launch_combine_t<D, true, false>(items, grid, max_splits, a, s);
-  if (a.part_bf16) return launch_combine_t<D, false, true>(items, grid, max_splits, a, s);
-  return launch_combine_t<D, false, false>(items, grid, max_splits, a, s);
+  if (a.out_f32 && a.part_bf16) return launch_combine_t<D, true, true>(items, n, max_rows, max_splits, a, s);
+  if (a.out_f32) return launch_combine_t<D, true, false>(items, n, max_rows, max_splits, a, s);
+  if (a.part_bf16) return launch_combine_t<D, false, true>(items, n, max_rows, max_splits, a, s);
+  return launch_combine_t<D, false, false>(items, n, max_rows, max_splits, a, s);
 }
 
 }  // namespace
@@ -378,10 +455,8 @@ hipError_t launch_decode(const WorkItem* items, int num_items, const AttnArgs& a
 hipError_t launch_combine(const CombineItem* items, int num_items, int max_rows, int max_splits,
                           const AttnArgs& a, int head_dim, hipStream_t stream) {
   if (num_items == 0) return hipSuccess;
-  const int threads = max_rows * (head_dim / 8);
-  const dim3 grid(num_items, (threads + 255) / 256);
-  if (head_dim == 128) return launch_combine_d<128>(items, grid, max_splits, a, stream);
-  if (head_dim == 64) return launch_combine_d<64>(items, grid, max_splits, a, stream);
+  if (head_dim == 128) return launch_combine_d<128>(items, num_items, max_rows, max_splits, a, stream);
+  if (head_dim == 64) return launch_combine_d<64>(items, num_items, max_rows, max_splits, a, stream);
   return hipErrorInvalidValue;
 }
 

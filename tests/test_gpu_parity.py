@@ -135,6 +135,36 @@ def test_forced_splits_agree(H):
         assert np.abs(o - outs[0]).max() <= 1e-2
 
 
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_many_splits_per_tile(H, out_dtype):
+    """Tiles split more than 8 ways take the combine whose threads (2, 4 or
+    8 per row) share the splits of a row: a 64-token chunk over an 8000-key
+    prefix at the 4-head d = 64 shape (63 splits per row tile), decode rows
+    cut into 64-key splits
+    (up to 141, several batches per thread), and one plan with both kinds
+    (a 70-way prefill tile beside decode rows of 1-3 splits: two combine
+    launches, one per kind), and 12- and 24-way splits. Every row against
+    the oracle, bf16 and fp32."""
+    b = make(seed=21, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+             query_lens=[64], seq_lens=[8064])
+    db = run_and_compare(H, b, f"63-way split d64 out={out_dtype}", out_dtype)
+    info = db.plan.info()
+    assert info["num_combine_items"] == 4 and info["num_prefill_items"] >= 4 * 60
+    b = make(seed=22, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
+             query_lens=[1, 1, 1], seq_lens=[9000, 700, 4100])
+    run_and_compare(H, b, f"decode split 64 (141 splits) out={out_dtype}", out_dtype,
+                    options={"decode_split_keys": 64})
+    b = make(seed=23, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
+             query_lens=[1, 1, 40], seq_lens=[1300, 129, 5000])
+    run_and_compare(H, b, f"mixed: 70-way prefill tile + decode rows out={out_dtype}", out_dtype,
+                    options={"prefill_split": 70})
+    b = make(seed=24, num_q_heads=4, num_kv_heads=4, head_dim=64, page_size=16,
+             query_lens=[100], seq_lens=[3000])
+    for split in (12, 24):          # 2 and 4 threads per row in the combine
+        run_and_compare(H, b, f"{split}-way split d64 out={out_dtype}", out_dtype,
+                        options={"prefill_split": split})
+
+
 def test_decode_split_sizes_agree(H):
     b = make(seed=8, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=128,
              query_lens=[1, 1, 1], seq_lens=[5000, 129, 2048])
