@@ -81,7 +81,8 @@ hipError_t launch_prefill(const WorkItem* items, int num_items,
 hipError_t launch_decode(const WorkItem* items, int num_items,
                          const AttnArgs& a, int head_dim, int group,
                          hipStream_t stream);
-// max_rows / max_splits: the largest rows and nsplit over the items.
+// max_rows / max_splits: the largest rows and nsplit over the items; up to
+// 8 splits one thread folds a row's splits, beyond that 2-8 threads share them.
 hipError_t launch_combine(const CombineItem* items, int num_items,
                           int max_rows, int max_splits, const AttnArgs& a,
                           int head_dim, hipStream_t stream);

@@ -13,7 +13,8 @@
 //   * each thread keeps U keys' K and V loads in flight before using them;
 //   * partial (max, sum, O) of the 16 key slots are merged in registers and
 //     LDS; long rows are split over several items and merged by
-//     combine_kernel (log-sum-exp weights).
+//     combine_kernel, or combine_wide_kernel past 8 splits (log-sum-exp
+//     weights).
 #include <math.h>
 
 #include <type_traits>
