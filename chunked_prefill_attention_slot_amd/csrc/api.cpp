@@ -45,7 +45,13 @@ constexpr int kNumXcds = 8;
 // products): a tile is split only when that shortens the longest item by
 // more.
 constexpr int kCombineTiles = 2;
-constexpr int kDefaultDecodeSplit = 512;
+// Default keys per decode split: the largest of these that still gives
+// every CU kDecodeItemsPerCu decode items, else the smallest. Longer
+// splits mean fewer item starts and merges (the LLaMA-13B decode rows run
+// 1.5% faster at 2048 than at 512 keys), shorter ones fill the GPU when
+// the decode rows are few.
+constexpr int kDecodeSplitChoices[] = {2048, 1024, 512, 256};
+constexpr int kDecodeItemsPerCu = 4;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -464,7 +470,15 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
     fits = fits && add_split(p, p->prefill, t, nsplit, cpa::kSplitAlign);
   }
 
-  const int dsk = opt.decode_split_keys > 0 ? opt.decode_split_keys : cpa::kDefaultDecodeSplit;
+  int dsk = opt.decode_split_keys;
+  if (dsk <= 0) {
+    for (int cand : cpa::kDecodeSplitChoices) {
+      dsk = cand;
+      int64_t items = 0;
+      for (int32_t s : decode_seqs) items += ((int64_t)seq_lens[s] + cand - 1) / cand * Hkv;
+      if (items >= (int64_t)cpa::kDecodeItemsPerCu * cus) break;
+    }
+  }
   std::vector<int32_t> qsl((size_t)num_seqs + 1, 0);
   for (int32_t s = 0; s < num_seqs; ++s) qsl[s + 1] = qsl[s] + query_lens[s];
   for (int32_t s : decode_seqs) {

@@ -121,7 +121,9 @@ typedef struct cpa_plan_options {
   int32_t num_cus;          /* compute units to plan for (default 256) */
   int32_t prefill_split;    /* force this many key splits per prefill
                                tile (default: chosen from the work) */
-  int32_t decode_split_keys;/* keys per decode split (default 512) */
+  int32_t decode_split_keys;/* keys per decode split (default: the largest
+                               of 2048, 1024, 512 that still gives 4 decode
+                               items per CU, else 256) */
   int32_t min_split_keys;   /* smallest prefill split piece in keys, a
                                multiple of 64; nonzero also keeps splits
                                that the planner's cost rule would drop

@@ -215,9 +215,26 @@ def test_plan_refuses_oversized_plans(cpa):
     with pytest.raises(cpa.CpaError) as e:
         cpa.cpa_plan_create(d, [1] * 64, [32768] * 64, {"decode_split_keys": 1})
     assert e.value.status == cpa.CPA_ERR_UNSUPPORTED and "too large" in cpa.cpa_last_error()
-    # the same batch with the default split is fine
+    # the same batch with the default split (2048 keys here) is fine
     assert cpa.cpa_plan_create(d, [1] * 64, [32768] * 64).info()["num_decode_items"] == \
-        64 * 40 * 64
+        64 * 40 * 16
+
+
+def test_default_decode_split_fills_the_cus(cpa):
+    """Without decode_split_keys the planner takes the largest split of 2048,
+    1024, 512 keys that gives at least 4 decode items per CU (256 CUs), else
+    256; an explicit value is used as given."""
+    d = desc(cpa, num_q_heads=40, num_kv_heads=40, num_blocks=40000, max_blocks_per_seq=256)
+    def items(ql, sl, opts=None):
+        return cpa.cpa_plan_create(d, ql, sl, opts).info()["num_decode_items"]
+    n = [1024 + 457 * i for i in range(16)]           # 16 rows, 1024 .. 7879 keys
+    per = lambda k: sum((x + k - 1) // k for x in n) * 40
+    assert per(2048) >= 1024 and items([1] * 16, n) == per(2048)
+    # 2 rows of 4096 keys: 2048 -> 160 items, 1024 -> 320, 512 -> 640, so 256
+    assert items([1, 1], [4096, 4096]) == 2 * 40 * 16
+    # 6 rows of 3000 keys: 1024 gives 720, 512 gives 1440 (>= 1024)
+    assert items([1] * 6, [3000] * 6) == 6 * 40 * 6
+    assert items([1] * 16, n, {"decode_split_keys": 512}) == per(512)
 
 
 def test_plan_page_cap_splits(cpa):
