@@ -43,8 +43,13 @@ constexpr int kNumXcds = 8;
 // about as much as two 64-key tiles of one item (at d = 64 and d = 128
 // alike: a lone item's tiles are bound by memory latency, not by the
 // products): a tile is split only when that shortens the longest item by
-// more.
+// more. In the d = 64 kernel, an item of at most 64 packed rows has six
+// of its eight waves idle (they skip their phases), so its tiles cost about
+// half as much and the split must save twice as many of them: measured,
+// 4-tile items of 32-64 rows ran 0.25-0.35 us faster unsplit, 5-tile items
+// tied, and items of 96-128 rows or of 6+ tiles still gained from the split.
 constexpr int kCombineTiles = 2;
+constexpr int kSmallItemRows = 64;
 // Default keys per decode split: the largest of these that still gives
 // every CU kDecodeItemsPerCu decode items, else the smallest. Longer
 // splits mean fewer item starts and merges (the LLaMA-13B decode rows run
@@ -446,9 +451,11 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   int64_t chunk_keys = page_cap_keys;
   if (opt.prefill_split == 0 && (int64_t)tiles.size() < target && !tiles.empty()) {
     int64_t total_keys = 0, longest = 0;
+    int max_rows = 0;
     for (const Tile& t : tiles) {
       total_keys += t.kv_len;
       longest = std::max<int64_t>(longest, t.kv_len);
+      max_rows = std::max(max_rows, t.nq * t.nheads);
     }
     int64_t c = (int64_t)cpa::round_up((size_t)((total_keys + target - 1) / target),
                                        cpa::kSplitAlign);
@@ -460,7 +467,10 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
     };
     while (count(c) > target) c += cpa::kSplitAlign;
     const int64_t tiles_unsplit = (longest + cpa::kSplitAlign - 1) / cpa::kSplitAlign;
-    if (opt.min_split_keys > 0 || tiles_unsplit - c / cpa::kSplitAlign > cpa::kCombineTiles)
+    const int64_t combine_tiles = (desc->head_dim == 64 && max_rows <= cpa::kSmallItemRows)
+                                      ? 2 * cpa::kCombineTiles
+                                      : cpa::kCombineTiles;
+    if (opt.min_split_keys > 0 || tiles_unsplit - c / cpa::kSplitAlign > combine_tiles)
       chunk_keys = std::min(chunk_keys, c);
   }
   bool fits = true;

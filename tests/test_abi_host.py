@@ -181,7 +181,8 @@ def test_plan_counts_and_pairs(cpa):
 def test_plan_splits_short_ranges_only_when_it_pays(cpa):
     """Tiles too few to fill the CUs are split into pieces as short as one
     64-key tile, but only when that shortens the longest item by more than
-    the combine launch costs (two tiles)."""
+    the combine launch costs (two tiles; four for d = 64 items of at most 64
+    rows, whose tiles cost about half)."""
     d = desc(cpa)
     # Llama-3-8B chunk at H = 0: 64 tiles of 64 + 64t keys; 128-key pieces
     # (2 tiles, down from 8) give 8 * (1+1+2+2+3+3+4+4) = 160 items.
@@ -206,6 +207,14 @@ def test_plan_splits_short_ranges_only_when_it_pays(cpa):
         assert cpa.cpa_plan_create(tiny, [n], [n]).info()["num_prefill_items"] <= 256
     with pytest.raises(cpa.CpaError):
         cpa.cpa_plan_create(tiny, [128], [128], {"min_split_keys": 100})
+    # d = 64 items of at most 64 rows (six of eight waves idle) need twice
+    # the saving: 4 or 5 tiles stay whole, 6 tiles split; 128 rows and the
+    # d = 128 kernel keep the two-tile rule
+    for c, h, items in ((64, 192, 4), (64, 256, 4), (32, 224, 4), (64, 320, 24), (128, 128, 16)):
+        assert cpa.cpa_plan_create(tiny, [c], [c + h]).info()["num_prefill_items"] == items, (c, h)
+    d128 = desc(cpa, num_q_heads=4, num_kv_heads=4, head_dim=128, page_size=16,
+                num_blocks=4096, max_blocks_per_seq=2100)
+    assert cpa.cpa_plan_create(d128, [64], [256]).info()["num_prefill_items"] == 16
 
 
 def test_plan_refuses_oversized_plans(cpa):
