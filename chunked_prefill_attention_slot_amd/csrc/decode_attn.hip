@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const WorkItem* __restrict_
   constexpr int LPK = D / 8;      // lanes per key
   constexpr int KPW = 64 / LPK;   // keys per wave step
   constexpr int KPB = 4 * KPW;    // keys per block step
-  constexpr int U = (G >= 8) ? 4 : 8;  // block steps loaded before use
+  constexpr int U = (G >= 8) ? 4 : (G == 1 ? 16 : 8);  // block steps loaded before use
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ __attribute__((aligned(16))) float s_o[4][G][D];
 
