@@ -34,7 +34,8 @@ and one object per further leg (all run by default; --legs selects):
   predictor    -- dynamic chunking at the 4/4-head d=64 shape: 64 profiled
                   sizes, quadratic fit, T, the 32768-token walk at align 128
                   and 16 with per-chunk ratios to T and to the model, and
-                  an online-calibrated walk;
+                  two online-calibrated walks (the record window seeded
+                  with the profile's runs, and unseeded);
   chunk_schedule -- the token-budget step loop under fixed 512, progressive
                   [2048, 1024, 512], predictor and calibrated chunk rules
                   (a 16-request stream and one 32768-token prompt), and the
