@@ -192,9 +192,10 @@ cpa_status cpa_plan_upload(cpa_plan plan, void* workspace,
  *   out: device [T, Hq, d], bf16 or fp32 per desc->out_dtype.
  *   workspace: the buffer passed to cpa_plan_upload for this plan.
  * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax. Rows
- * whose keys were split over several work items are merged by a second
- * kernel from partials kept in the output's precision (bf16 or fp32), with
- * fp32 max and sum.
+ * whose keys were split over several work items are merged by a later
+ * kernel (one launch for split prefill tiles, one for split decode rows)
+ * from partials kept in the output's precision (bf16 or fp32), with fp32
+ * max and sum.
  */
 cpa_status cpa_attention(cpa_plan plan, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_table,
