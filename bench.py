@@ -520,6 +520,39 @@ def seed_calibration(calib, sizes, ms):
         calib.record(cpa.cpa_calib_features([int(l)], [0]), float(m))
 
 
+def online_walk(calib, cfg, fit, prompt, measure):
+    """Prefill `prompt` tokens with chunks sized by the online calibration
+    (dynamic-chunking design, "online calibration"): each chunk solves the
+    current two-variable model for T' = f(base, 0) of that model (R22),
+    falling back to the profiled one-variable predictor while the window
+    holds no model; measure(L, chunk) -> ms runs and times the chunk, whose
+    features and time are recorded before the next solve. Returns the rows
+    (L, chunk, ms, T' used) and the number of refused refits."""
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    a, b, c = fit
+    T = cpa.cpa_predictor_target(cfg, a, b)
+    f_base = a * 2048.0 * 2048.0 + b * 2048.0 + c
+    rows, refused, L = [], 0, 0
+    while L < prompt:
+        try:
+            a2, b2, c2 = calib.model()
+            T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
+            ch, _ = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
+        except cpa.CpaError:
+            T2 = f_base
+            ch, _ = cpa.cpa_predictor_next_chunk(cfg, a, b, T, L, prompt - L)
+        if ch <= 0:
+            break
+        m = measure(L, ch)
+        try:
+            calib.record(cpa.cpa_calib_features([ch], [L]), m)
+        except cpa.CpaError:
+            refused += 1       # window does not determine the model (e.g. one chunk size)
+        rows.append((L, ch, m, T2))
+        L += ch
+    return rows, refused
+
+
 def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
     """The dynamic-chunking workload: profile the fused KV write + attention
     at 64 sizes (2048 down to 32, H = 0), fit f(l) = a l^2 + b l + c, set
@@ -566,31 +599,14 @@ def predictor_run(args, shape="tiny", prompt=32768, aligns=(128, 16)):
 
     # Online calibration of f(C, H) = a*C*(C+H) + b*(C+H) + c over the same prompt.
     cfg = cpa.predictor_cfg(align=aligns[0])
-    T = cpa.cpa_predictor_target(cfg, a, bb)
     f_base = a * 2048.0 * 2048.0 + bb * 2048.0 + c
     for key, seeded in (("online", True), ("online_unseeded", False)):
         calib = cpa.Calib(min_points=5, window=30)
         if seeded:
             seed_calibration(calib, sizes, ms)
-        online, refused = [], 0
-        L = 0
-        while L < prompt:
-            try:
-                a2, b2, c2 = calib.model()
-                T2 = cpa.cpa_calib_target(cfg, a2, b2, c2)
-                ch, x = cpa.cpa_calib_next_chunk(cfg, a2, b2, c2, T2, L, prompt - L)
-            except cpa.CpaError:
-                T2 = f_base
-                ch, x = cpa.cpa_predictor_next_chunk(cfg, a, bb, T, L, prompt - L)
-            if ch <= 0:
-                break
-            m = median_ms(runner(L, ch), 11, 2)["median_ms"]
-            try:
-                calib.record(cpa.cpa_calib_features([ch], [L]), m)
-            except cpa.CpaError:
-                refused += 1       # window does not determine the model (e.g. one chunk size)
-            online.append((L, ch, m, T2))
-            L += ch
+        online, refused = online_walk(
+            calib, cfg, (a, bb, c), prompt,
+            lambda L, ch: median_ms(runner(L, ch), 11, 2)["median_ms"])
         try:
             fin = list(calib.model())
         except cpa.CpaError:

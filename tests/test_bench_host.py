@@ -47,3 +47,40 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_online_walk_needs_the_seed_on_a_latency_floor():
+    """A synthetic chunk latency shaped like the 4-head d = 64 workload: a
+    per-call cost that saturates with the chunk size (so the profile at
+    H = 0 is concave and its quadratic fit has a < 0) plus a cost per
+    (query, key) pair and per prefix key. Unseeded, the online walk repeats
+    the profile model's one chunk size and every refit is refused; seeded
+    with the profile's runs, it has a model from the first chunk, the chunks
+    shrink as the prefix grows, and the chunk latencies spread less."""
+    import math
+    import numpy as np
+    from chunked_prefill_attention_slot_amd import binding as cpa
+    from oracle.predictor import profile_sizes
+
+    def lat(C, H):    # ms
+        return 0.0065 + 0.0105 * (1.0 - math.exp(-C / 400.0)) + 1.0e-9 * C * H + 3e-7 * H
+
+    sizes = profile_sizes(2048, 64, 32)
+    ms = [lat(l, 0) for l in sizes]
+    fit = cpa.cpa_predictor_fit(sizes, ms)
+    assert fit[0] < 0                              # concave profile: degenerate model
+    cfg = cpa.predictor_cfg(align=128)
+    bare = cpa.Calib(min_points=5, window=30)
+    rows, refused = bench.online_walk(bare, cfg, fit, 32768, lat)
+    chunks = [ch for _, ch, _, _ in rows]
+    # one size throughout (the last chunk is the remainder); every refit
+    # from the fifth record on is refused but the one the remainder allows
+    assert len(set(chunks[:-1])) == 1 and refused >= len(rows) - 5
+    seeded = cpa.Calib(min_points=5, window=30)
+    bench.seed_calibration(seeded, sizes, ms)
+    rows2, refused2 = bench.online_walk(seeded, cfg, fit, 32768, lat)
+    chunks2 = [ch for _, ch, _, _ in rows2]
+    assert refused2 < len(rows2) // 2
+    assert len(set(chunks2)) >= 4 and max(chunks2[-10:]) < chunks2[0]
+    cv = lambda v: float(np.std(v) / np.mean(v))
+    assert cv([m for _, _, m, _ in rows2]) < cv([m for _, _, m, _ in rows])
