@@ -77,6 +77,9 @@ SHAPES = [
     (40, 40, 128, 128, [1] * 4 + [129], [700, 129, 2000, 4100, 1000]),
     (12, 4, 128, 64, [3, 0, 2], [3, 9, 300]),         # tiny chunks, empty row
     (32, 2, 128, 16, [1, 1], [100, 1000]),            # decode GQA 16 -> MFMA kernel
+    (48, 8, 128, 32, [1, 70, 1], [64, 300, 2000]),    # GQA 6: two heads per tile
+    (128, 1, 64, 16, [1, 3, 40], [500, 3, 900]),      # GQA 128: two queries per tile
+    (256, 1, 64, 16, [2, 1], [40, 700]),              # GQA 256: one query per tile
 ]
 
 
@@ -86,6 +89,45 @@ def test_random_shapes(H, shape):
     b = make(seed=sum(sl) % 1000, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
              page_size=P, query_lens=ql, seq_lens=sl, extra_pages=2)
     run_and_compare(H, b, f"shape {shape}")
+
+
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random batches: GQA ratio, head size, page size, a mix of
+    decode rows, prefill chunks and empty rows over random prefixes, and a
+    random plan option (forced prefill splits, decode split size, split
+    floor, a small item target) and output precision."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16, 32]))
+        while hkv * g > 64:
+            hkv //= 2
+        d = int(rng.choice([64, 128]))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
+        ql, sl = [], []
+        for _ in range(int(rng.integers(1, 6))):
+            kind = rng.choice(["decode", "prefill", "prefill", "empty"])
+            q = {"decode": 1, "empty": 0}.get(kind) or int(rng.integers(2, 300))
+            h = int(rng.integers(0, 1500)) if rng.random() < 0.8 else 0
+            ql.append(q)
+            sl.append(max(q + h, 1))
+        opt = [None, {"prefill_split": int(rng.integers(2, 9))},
+               {"decode_split_keys": 64 * int(rng.integers(1, 9))},
+               {"min_split_keys": 64 * int(rng.integers(1, 5))},
+               {"target_items": int(rng.integers(8, 64))}][int(rng.integers(0, 5))]
+        cases.append((i, hkv * g, hkv, d, P, ql, sl, opt, int(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: str(c[0]))
+def test_seeded_sweep(H, case):
+    i, hq, hkv, d, P, ql, sl, opt, out_dtype = case
+    if sum(ql) == 0:
+        ql[0], sl[0] = 1, max(sl[0], 1)
+    b = make(seed=100 + i, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=P,
+             query_lens=ql, seq_lens=sl, extra_pages=2)
+    run_and_compare(H, b, f"sweep {case}", out_dtype=out_dtype, options=opt)
 
 
 @pytest.mark.parametrize("shift", [(0.0, 0.0), (2.5, 2.5), (2.5, -2.5)])
@@ -111,6 +153,22 @@ def test_large_scores(H, shift):
         db = H.DeviceBatch(b, out_dtype=1, options=opts)
         db.run()
         H.compare(db.out_f64(), ref, f"{label} {opts}")
+
+
+def test_all_rows_empty(H):
+    """A batch whose every chunk is empty: each entry point succeeds without
+    touching the caches or launching work."""
+    b = make(seed=15, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+             query_lens=[0, 0], seq_lens=[5, 300], extra_pages=1)
+    banner("all rows empty")
+    db = H.DeviceBatch(b)
+    assert db.plan.info()["num_tokens"] == 0
+    db.run()
+    db.kv_write_attention()
+    torch.cuda.synchronize()
+    assert db.out.numel() == 0
+    np.testing.assert_array_equal(H.from_dev_u16(db.k_cache), b.k_cache)
+    np.testing.assert_array_equal(H.from_dev_u16(db.v_cache), b.v_cache)
 
 
 def test_page_cap_split(H):
