@@ -10,8 +10,9 @@
 //     combine item;
 //   * decode rows (query_len == 1): one item per (sequence, KV head, key
 //     range of decode_split_keys), merged by a combine item when split.
-// Items are ordered longest key range first so the tail of the grid holds
-// the short ones.
+// Items are then ordered for the XCDs (order_for_xcds): each (sequence,
+// KV head) group on one XCD, the groups balanced over the XCDs, the
+// costliest items of an XCD first.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
