@@ -171,6 +171,35 @@ def test_all_rows_empty(H):
     np.testing.assert_array_equal(H.from_dev_u16(db.v_cache), b.v_cache)
 
 
+@pytest.mark.parametrize("shape", [
+    # hq, hkv, d, P, query_lens, seq_lens (prefixes end inside pages; decode
+    # rows of the decode kernel and of the MFMA kernel; an empty row)
+    (32, 8, 128, 128, [300, 1, 1, 0], [1000, 77, 3000, 5]),
+    (16, 1, 64, 16, [45, 1], [333, 100]),
+    (8, 8, 64, 64, [1, 130], [65, 130]),
+])
+def test_nan_in_unused_slots(H, shape):
+    """Every cache slot that no sequence position maps to holds a NaN bit
+    pattern: keys past a range and the tail of a page must never reach a
+    product (0 * NaN would poison the row)."""
+    hq, hkv, d, P, ql, sl = shape
+    b = make(seed=41, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=P,
+             query_lens=ql, seq_lens=sl, extra_pages=3)
+    used = np.zeros(b.num_blocks * P, dtype=bool)
+    for s_, n in enumerate(sl):
+        pos = np.arange(n)
+        used[b.block_table[s_, pos // P].astype(np.int64) * P + pos % P] = True
+    nan_bits = np.uint16(0x7FC0)
+    for cache in (b.k_cache, b.v_cache):
+        flat = cache.transpose(0, 2, 1, 3).reshape(b.num_blocks * P, hkv, d)
+        flat[~used] = nan_bits
+        cache[...] = flat.reshape(b.num_blocks, P, hkv, d).transpose(0, 2, 1, 3)
+    assert np.isnan((b.k_cache.astype(np.uint32) << 16).view(np.float32)).any()
+    for opts in (None, {"prefill_split": 1}):
+        db = run_and_compare(H, b, f"NaN in unused slots {shape} {opts}", options=opts)
+        assert np.isfinite(db.out_f64()).all()
+
+
 def test_page_cap_split(H):
     """Maximum item size: one sequence of 40000 keys in 16-key pages (2500
     block-table entries, over the 2047 one item stages), splitting turned
