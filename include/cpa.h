@@ -35,8 +35,11 @@
  *   - bf16 tensors are raw 16-bit bfloat16 bit patterns, row-major,
  *     contiguous, 16-byte aligned.
  *   - Contents of device index arrays (slot_mapping, block_table) are
- *     trusted for speed; kernels skip slots and pages outside the cache
- *     instead of faulting. cpa_validate_metadata checks them on the host.
+ *     trusted for speed, and the kernels never touch memory outside the
+ *     cache for them: a slot outside [0, num_blocks * page_size) is not
+ *     written, and a key whose block-table entry lies outside
+ *     [0, num_blocks) reads as zero K and V rows (score 0, so it still takes
+ *     part in the softmax). cpa_validate_metadata checks them on the host.
  */
 #ifndef CPA_H_
 #define CPA_H_

@@ -37,14 +37,17 @@ def test_kv_write_bit_exact(H, case):
     from oracle.kv_cache import kv_write
     b = make(**case)
     sm = b.slot_mapping.copy()
+    ref_sm = sm.copy()
     if b.num_tokens > 3:
-        sm[2] = -1                       # a padding token: skipped
+        sm[2] = ref_sm[2] = -1           # a padding token: skipped
+        sm[1] = b.num_blocks * b.page_size + 5   # outside the cache: not written
+        ref_sm[1] = -1
         b.slot_mapping = sm
     banner(f"kv_write {case}")
     db = H.DeviceBatch(b)
     db.kv_write()
     torch.cuda.synchronize()
-    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.page_size)
+    kc, vc = kv_write(b.k_cache, b.v_cache, b.k_new, b.v_new, ref_sm, b.page_size)
     np.testing.assert_array_equal(H.from_dev_u16(db.k_cache), kc)
     np.testing.assert_array_equal(H.from_dev_u16(db.v_cache), vc)
 
@@ -198,6 +201,46 @@ def test_nan_in_unused_slots(H, shape):
     for opts in (None, {"prefill_split": 1}):
         db = run_and_compare(H, b, f"NaN in unused slots {shape} {opts}", options=opts)
         assert np.isfinite(db.out_f64()).all()
+
+
+@pytest.mark.parametrize("shape", [
+    (32, 8, 128, 128, [300, 1], [1800, 700]),     # prefill chunk, decode row (decode kernel)
+    (16, 1, 64, 16, [40, 1], [400, 300]),         # MQA: decode row through the MFMA kernel
+])
+def test_pages_outside_the_cache_read_as_zero(H, shape):
+    """Block-table entries of cached (prefix) pages set outside [0,
+    num_blocks): the kernels' bounds checks read those keys as zero K and V
+    rows (score 0, still in the softmax) instead of touching memory. The
+    oracle sees the same batch with those entries pointing at an all-zero
+    page; fused and separate calls alike."""
+    from tests.gpu_helpers import DeviceBatch
+    hq, hkv, d, P, ql, sl = shape
+    b = make(seed=43, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=P,
+             query_lens=ql, seq_lens=sl, extra_pages=2)
+    bad = [b.num_blocks + 3, -2, 1 << 30]
+    ref_bt = b.block_table.copy()
+    k = 0
+    for s_, (q, n) in enumerate(zip(ql, sl)):
+        for pg in range(0, (n - q) // P, 3):          # whole pages of the prefix only
+            b.block_table[s_, pg] = bad[k % 3]
+            ref_bt[s_, pg] = b.num_blocks              # the appended zero page
+            k += 1
+    assert k > 0
+    import copy
+    r = copy.copy(b)
+    zero = np.zeros((1,) + b.k_cache.shape[1:], dtype=b.k_cache.dtype)
+    r.k_cache = np.concatenate([b.k_cache, zero])
+    r.v_cache = np.concatenate([b.v_cache, zero])
+    r.block_table = ref_bt
+    ref = H.oracle_out(r)
+    banner(f"pages outside the cache {shape}")
+    db = DeviceBatch(b)
+    db.run()
+    H.compare(db.out_f64(), ref, f"pages outside the cache {shape} separate")
+    db2 = DeviceBatch(b)
+    db2.kv_write_attention()
+    torch.cuda.synchronize()
+    H.compare(db2.out_f64(), ref, f"pages outside the cache {shape} fused")
 
 
 def test_page_cap_split(H):
