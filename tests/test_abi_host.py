@@ -539,3 +539,36 @@ def test_fused_call_rejects_null_pointers(cpa):
         assert st == cpa.CPA_ERR_INVALID_ARG, hole
         assert "NULL" in cpa.cpa_last_error()
     p.destroy()
+
+
+def test_host_entry_points_from_many_threads(cpa):
+    """Plans, their info, refusals (with per-thread messages) and predictor
+    calls from eight host threads at once give the single-thread results."""
+    import threading
+    desc = cpa.layer_desc(32, 8, 128, 128, 200, 104)
+    bad = cpa.layer_desc(32, 8, 96, 128, 200, 104)
+    want = cpa.cpa_plan_create(desc, [512, 1, 40], [12800, 700, 300]).info()
+    cfg = cpa.predictor_cfg(align=128)
+    want_chunk = cpa.cpa_predictor_next_chunk(cfg, 2e-9, 5e-6, 0.0125, 4096, 30000)
+    errors = []
+
+    def work(seed):
+        try:
+            for i in range(200):
+                p = cpa.cpa_plan_create(desc, [512, 1, 40], [12800, 700, 300])
+                assert p.info() == want
+                p.destroy()
+                with pytest.raises(cpa.CpaError) as e:
+                    cpa.cpa_plan_create(bad, [512], [12800])
+                assert "head_dim" in str(e.value)
+                assert cpa.cpa_predictor_next_chunk(cfg, 2e-9, 5e-6, 0.0125, 4096,
+                                                    30000) == want_chunk
+        except Exception as ex:  # reported below, on the main thread
+            errors.append(repr(ex))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
