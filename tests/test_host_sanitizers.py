@@ -67,3 +67,32 @@ def test_host_abi_tests_under_sanitizers(built):
     assert r.returncode == 0, out
     assert "runtime error" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr, out
     assert " passed" in r.stdout, out
+
+
+def test_host_entry_points_under_thread_sanitizer():
+    """tests/sanitize/host_threads.cpp under ThreadSanitizer: eight threads
+    create, inspect, upload (to their own and to one shared workspace, which
+    exercises the process-wide workspace registry) and destroy plans, hit
+    refusals, and run the predictor, the calibration and the batch former;
+    any data race fails the run."""
+    if shutil.which("make") is None or not tsan_available():
+        pytest.skip("needs make and g++ with ThreadSanitizer")
+    r = subprocess.run(["make", "-C", SAN, "-j8", "tsan"], capture_output=True, text=True,
+                       timeout=900)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1")
+    r = subprocess.run([os.path.join(SAN, "_build_tsan", "host_threads")], capture_output=True,
+                       text=True, timeout=600, env=env)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-6000:]
+    assert "ThreadSanitizer" not in r.stderr, r.stderr[-6000:]
+    assert "host threads ok" in r.stdout
+
+
+def tsan_available():
+    try:
+        r = subprocess.run(["g++", "-print-file-name=libtsan.so"], capture_output=True,
+                           text=True, timeout=60)
+    except OSError:
+        return False
+    path = r.stdout.strip()
+    return os.path.isabs(path) and os.path.exists(path)
