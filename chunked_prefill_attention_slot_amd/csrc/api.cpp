@@ -132,6 +132,7 @@ struct cpa_plan_s {
   // to 256, and one grid for both would be mostly empty blocks).
   int32_t combine_count[2] = {0, 0}, combine_rows[2] = {0, 0}, combine_splits[2] = {0, 0};
   int32_t part_bf16 = 0;         // split partials O/l in bf16 (else fp32)
+  int32_t prefill_max_rows = 0;  // largest nq * nheads of a prefill item
   int64_t visible_pairs = 0;
   std::vector<cpa::WorkItem> prefill, decode;
   std::vector<cpa::CombineItem> combine;
@@ -330,7 +331,8 @@ cpa_status attention_impl(cpa_plan plan, const void* q, const void* k_cache, con
     }
   }
   e = cpa::launch_prefill(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_prefill),
-                          (int)plan->prefill.size(), a, d.head_dim, fused, stream);
+                          (int)plan->prefill.size(), a, d.head_dim, fused,
+                          plan->prefill_max_rows, stream);
   if (e != hipSuccess) return cpa::hip_fail(e, "prefill attention launch");
   e = cpa::launch_decode(reinterpret_cast<const cpa::WorkItem*>(ws + plan->off_decode),
                          (int)plan->decode.size(), a, d.head_dim, plan->decode_group, stream);
@@ -509,6 +511,8 @@ cpa_status cpa_plan_create(const cpa_layer_desc* desc, const int32_t* query_lens
   }
   order_for_xcds(p->prefill, cpa::kNumXcds);
   order_for_xcds(p->decode, cpa::kNumXcds);
+  for (const cpa::WorkItem& w : p->prefill)
+    p->prefill_max_rows = std::max(p->prefill_max_rows, w.nq * w.nheads);
 
   // Workspace: [zeros][prefill items][decode items][combine items][partial O][partial m,l]
   size_t off = cpa::kZeroBytes;

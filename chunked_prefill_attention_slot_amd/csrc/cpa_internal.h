@@ -75,9 +75,11 @@ constexpr int kFusedWritesPerThread = 4;
 
 // fused: also write the step's new K/V rows into the cache (the AttnArgs
 // k_new .. num_new_tokens fields), reading new keys from k_new / v_new.
+// max_rows: the largest nq * nheads over the items (small items let waves
+// without rows skip their work).
 hipError_t launch_prefill(const WorkItem* items, int num_items,
                           const AttnArgs& a, int head_dim, bool fused,
-                          hipStream_t stream);
+                          int max_rows, hipStream_t stream);
 hipError_t launch_decode(const WorkItem* items, int num_items,
                          const AttnArgs& a, int head_dim, int group,
                          hipStream_t stream);

@@ -152,7 +152,7 @@ __device__ __forceinline__ int v_swz(int r) {
   return (r & 3) << 1;
 }
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool SKIP>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
     const WorkItem* __restrict__ items, AttnArgs a) {
   using C = Cfg<D>;
@@ -175,12 +175,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int qi = r / it.nheads;
   const int hl = r - qi * it.nheads;
   const bool row_ok = qi < it.nq;
-  // A wave whose 32 packed rows all lie past the item's rows (a chunk
-  // shorter than the item) keeps only its share of the tile copies, the
-  // waits and the barriers, and leaves its SIMD to the partner wave. At
-  // d = 128 the test held across the loop costs scalar-register spills
-  // (16 -> 23) and slowed full items, so only the d = 64 kernel takes it.
-  const bool busy = D != 64 || 32 * w < it.nq * it.nheads;
+  // SKIP: a wave whose 32 packed rows all lie past the item's rows (a chunk
+  // shorter than the item, a decode row of a 16-head group) keeps only its
+  // share of the tile copies, the waits and the barriers, and leaves its
+  // SIMD to the partner wave. At d = 128 the test held across the loop
+  // costs scalar-register spills (16 -> 23) and slows full items, so the
+  // d = 128 kernel takes it in a separate instance, launched only when no
+  // item has more than 128 rows.
+  const bool busy = !SKIP || 32 * w < it.nq * it.nheads;
   const int qpos = it.hist + it.q0 + qi;
 
   // Q is copied into LDS first (buffers 2 and 3, which the first tile
@@ -785,17 +787,24 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
 }  // namespace
 
 hipError_t launch_prefill(const WorkItem* items, int num_items, const AttnArgs& a,
-                          int head_dim, bool fused, hipStream_t stream) {
+                          int head_dim, bool fused, int max_rows, hipStream_t stream) {
   if (num_items == 0) return hipSuccess;
   const dim3 block(64 * kPrefillWaves);
-  if (head_dim == 128 && fused)
-    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(num_items), block, 0, stream, items, a);
+  const dim3 grid(num_items);
+  // Items of at most 128 rows leave at least half the waves idle.
+  const bool small = max_rows <= kPrefillRows / 2;
+  if (head_dim == 128 && fused && small)
+    hipLaunchKernelGGL((prefill_kernel<128, true, true>), grid, block, 0, stream, items, a);
+  else if (head_dim == 128 && fused)
+    hipLaunchKernelGGL((prefill_kernel<128, true, false>), grid, block, 0, stream, items, a);
+  else if (head_dim == 128 && small)
+    hipLaunchKernelGGL((prefill_kernel<128, false, true>), grid, block, 0, stream, items, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(num_items), block, 0, stream, items, a);
+    hipLaunchKernelGGL((prefill_kernel<128, false, false>), grid, block, 0, stream, items, a);
   else if (head_dim == 64 && fused)
-    hipLaunchKernelGGL((prefill_kernel<64, true>), dim3(num_items), block, 0, stream, items, a);
+    hipLaunchKernelGGL((prefill_kernel<64, true, true>), grid, block, 0, stream, items, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3(num_items), block, 0, stream, items, a);
+    hipLaunchKernelGGL((prefill_kernel<64, false, true>), grid, block, 0, stream, items, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

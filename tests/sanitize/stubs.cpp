@@ -11,7 +11,7 @@
 
 namespace cpa {
 
-hipError_t launch_prefill(const WorkItem*, int, const AttnArgs&, int, bool, hipStream_t) {
+hipError_t launch_prefill(const WorkItem*, int, const AttnArgs&, int, bool, int, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_decode(const WorkItem*, int, const AttnArgs&, int, int, hipStream_t) {

@@ -69,9 +69,11 @@ def test_prefill_kernels_hold_two_waves_per_simd(resources):
 
 
 def test_fused_prefill_spills_stay_in_register_lanes(resources):
-    # The fused d = 128 kernel keeps a few scalar values in VGPR lanes; the
-    # loop was measured with 16 of them. More have slowed it by 5-14%.
-    for name, r in kernels(resources, r"prefill_kernelILi128ELb1E").items():
+    # The fused d = 128 kernel for full items keeps a few scalar values in
+    # VGPR lanes; its loop was measured with 16 of them. More have slowed it
+    # by 5-14%. (The instance for items of at most 128 rows, whose idle
+    # waves skip their work, is allowed more.)
+    for name, r in kernels(resources, r"prefill_kernelILi128ELb1ELb0E").items():
         assert r["SGPRs Spill"] <= 16, (name, r)
 
 
