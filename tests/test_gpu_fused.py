@@ -47,6 +47,12 @@ CASES = {
     "mha40_unfused": dict(seed=25, num_q_heads=40, num_kv_heads=40, head_dim=128,
                           page_size=128, query_lens=[512], seq_lens=[600],
                           rows={0: [0, 5, 88, 300, 511]}, options={"prefill_split": 1}),
+    # GQA 16 at d = 128: decode rows the decode kernel does not take and a
+    # 6-token chunk, every item at most 96 rows, so the launch takes the
+    # instance whose waves without rows skip their work
+    "gqa16_small_items": dict(seed=28, num_q_heads=64, num_kv_heads=4, head_dim=128,
+                              page_size=64, query_lens=[1, 1, 6], seq_lens=[700, 4100, 300],
+                              extra_pages=2),
     # the same batch with the planner's own splits: enough items to take
     # the writes in the prefill kernel
     "mha40_split": dict(seed=25, num_q_heads=40, num_kv_heads=40, head_dim=128,
