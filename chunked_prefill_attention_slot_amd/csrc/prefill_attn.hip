@@ -170,10 +170,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(
   const int n = lane & 31, hh = lane >> 5;
   const float sl2e = a.scale_log2e;
 
-  // This lane's query column: packed row r -> (query qi, head hl).
+  // This lane's query column: packed row r, of query qi.
   const int r = 32 * w + n;
   const int qi = r / it.nheads;
-  const int hl = r - qi * it.nheads;
   const bool row_ok = qi < it.nq;
   // SKIP: a wave whose 32 packed rows all lie past the item's rows (a chunk
   // shorter than the item, a decode row of a 16-head group) keeps only its
